@@ -1,0 +1,278 @@
+"""Benchmark of the FP8 hot path on one MI355X.
+
+One step = the forward pass of a 1.5B-class linear layer with hybrid-granularity
+FP8 (token-wise 1x128 E4M3 activations, 128x128-block E4M3 weights, UE8M0
+round-up scales) on seeded synthetic bf16 tensors already resident in HBM:
+  1. fp8_quantize_token  X [4096 x 1536] bf16 -> codes + scales
+  2. fp8_quantize_block  W [8960 x 1536] bf16 -> codes + scales
+  3. fp8_block_scaled_gemm  Y = Xq * Wq^T, M=4096 N=8960 K=1536, fp32 accumulate, bf16 out
+`value` is the whole step's throughput in TFLOP/s (2*M*N*K per step / step
+time).  Each kernel is also timed with events on the stream it runs on, and
+the dominant kernel (the GEMM) is reported against the dense FP8 MFMA peak.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
+
+Other workloads (--workload): dgrad7b, wgrad, mxstress -- for the per-kernel
+roofline figures; they print the same kind of JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, TFLOP/s
+METRIC = "FP8 quantize GB/s + block-scaled FP8 GEMM TFLOP/s, % of MI355X peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="fprop1p5b", choices=["fprop1p5b", "dgrad7b", "wgrad", "mxstress"])
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-rows", type=int, default=256, help="token rows in the oracle sample")
+    return p.parse_args()
+
+
+def to_dev(a):
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+class KernelTimer:
+    """Event pairs around each launch on the current stream; averages per kernel."""
+
+    def __init__(self):
+        self.pending = []
+        self.times = {}
+
+    def run(self, name, fn):
+        import torch
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn()
+        e.record()
+        self.pending.append((name, s, e))
+        return out
+
+    def collect(self):
+        for name, s, e in self.pending:
+            self.times.setdefault(name, []).append(s.elapsed_time(e) * 1e-3)
+        self.pending = []
+
+    def mean(self, name):
+        return float(np.mean(self.times[name]))
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    timer = KernelTimer()
+    for _ in range(warmup):
+        step(timer)
+    torch.cuda.synchronize()
+    timer.pending = []
+    timer.times = {}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timer.collect()
+    return wall / steps, timer
+
+
+# ----------------------------------------------------------------------- workloads
+
+def fprop_setup():
+    import synth
+    d = synth.fprop1p5b()
+    return {"x": to_dev(d["x"]), "w": to_dev(d["w"]), "host": d}
+
+
+def fprop_step_fn(t):
+    import torch
+    import mx_block_scaled_x128_amd as mx
+
+    def step(timer):
+        xq, xs = timer.run("quant_token_x", lambda: mx.quantize_token(t["x"], mx.E4M3, mx.ROW))
+        wq, ws = timer.run("quant_block_w", lambda: mx.quantize_block(t["w"], mx.E4M3))
+        timer.run("gemm", lambda: mx.block_scaled_gemm(xq, xs, mx.E4M3, wq, ws, mx.E4M3, mx.B_NK,
+                                                        mx.SCALE_BLOCK128, out_dtype=torch.bfloat16))
+    return step
+
+
+def cpu_baseline_fprop(host, rows):
+    """Oracle on a bounded sample: `rows` token rows of X through the token quantizer and
+    the GEMM, plus the whole weight quantizer; scaled to the full step."""
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    x, w = host["x"], host["w"]
+    M, K = x.shape
+    N = w.shape[0]
+    xs = np.ascontiguousarray(x[:rows])
+    t0 = time.perf_counter()
+    xq, xsc = oracle.quantize_rows(xs, oracle.E4M3, threads=threads)
+    t1 = time.perf_counter()
+    wq, wsc = oracle.quantize_block(w, oracle.E4M3, threads=threads)
+    t2 = time.perf_counter()
+    oracle.gemm(xq, xsc, oracle.E4M3, wq, wsc, oracle.E4M3, threads=threads)
+    t3 = time.perf_counter()
+    scale = M / float(rows)
+    t_step = (t1 - t0) * scale + (t2 - t1) + (t3 - t2) * scale
+    return {
+        "value": round(2.0 * M * N * K / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+        "kind": "oracle",
+        "sample": "%d of %d token rows through token quantization and the GEMM (fp64), full weight "
+                  "quantization; times scaled to the full step (%.1f s measured, %.1f s est. per step)"
+                  % (rows, M, t3 - t0, t_step),
+    }
+
+
+def bytes_token(rows, cols, in_bytes):
+    return rows * cols * (in_bytes + 1) + rows * ((cols + 127) // 128)
+
+
+def bytes_block(rows, cols, in_bytes):
+    return rows * cols * (in_bytes + 1) + ((rows + 127) // 128) * ((cols + 127) // 128)
+
+
+def bench_fprop(args):
+    import torch
+    t = fprop_setup()
+    M, K = t["x"].shape
+    N = t["w"].shape[0]
+    step = fprop_step_fn(t)
+    per_step, timer = time_steps(step, args.steps, args.warmup)
+    flops = 2.0 * M * N * K
+    g = timer.mean("gemm")
+    qx = timer.mean("quant_token_x")
+    qw = timer.mean("quant_block_w")
+    bx = bytes_token(M, K, 2)
+    bw = bytes_block(N, K, 2)
+    gemm_tflops = flops / g / 1e12
+    line = {
+        "metric": METRIC, "value": round(flops / per_step / 1e12, 3), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(per_step * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded numpy PCG64; bf16 inputs resident in HBM before timing)",
+        "config": {"workload": "fprop1p5b: token-quantize X 4096x1536 bf16 (1x128, E4M3) + block-quantize "
+                               "W 8960x1536 bf16 (128x128, E4M3) + block-scaled GEMM M=4096 N=8960 K=1536 "
+                               "bf16 out", "M": M, "N": N, "K": K, "global_batch": M, "parallelism": "single GPU"},
+        "kernels": {
+            "quant_token_x": {"us": round(qx * 1e6, 2), "GB/s": round(bx / qx / 1e9, 1),
+                              "frac_hbm_peak": round(bx / qx / 1e9 / HBM_PEAK_GBS, 4), "bytes": bx},
+            "quant_block_w": {"us": round(qw * 1e6, 2), "GB/s": round(bw / qw / 1e9, 1),
+                              "frac_hbm_peak": round(bw / qw / 1e9 / HBM_PEAK_GBS, 4), "bytes": bw},
+            "gemm": {"us": round(g * 1e6, 2), "TFLOP/s": round(gemm_tflops, 1),
+                     "frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "flops": flops},
+        },
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None},
+    }
+    line["cpu_baseline"] = None if args.no_cpu else cpu_baseline_fprop(t["host"], args.cpu_rows)
+    return line
+
+
+def bench_other(args):
+    """Per-kernel figures for the larger workloads (same JSON shape, kernels block filled)."""
+    import torch
+    import mx_block_scaled_x128_amd as mx
+    import synth
+    kern = {}
+    if args.workload == "dgrad7b":
+        d = synth.dgrad7b()
+        dy, w = to_dev(d["dy"]), to_dev(d["w"])
+        del d
+        M, K = dy.shape
+        N = w.shape[1]
+
+        def step(timer):
+            gq, gs = timer.run("quant_token_dy", lambda: mx.quantize_token(dy, mx.E5M2, mx.ROW))
+            wq, ws = timer.run("quant_block_w", lambda: mx.quantize_block(w, mx.E4M3))
+            timer.run("gemm", lambda: mx.block_scaled_gemm(gq, gs, mx.E5M2, wq, ws, mx.E4M3, mx.B_KN,
+                                                            mx.SCALE_BLOCK128, out_dtype=torch.bfloat16))
+        sizes = {"quant_token_dy": bytes_token(M, K, 2), "quant_block_w": bytes_block(K, N, 2)}
+        flops = 2.0 * M * N * K
+        desc = "dgrad7b: token-quantize dY 8192x18944 bf16 (E5M2) + block-quantize W 18944x3584 (E4M3) + GEMM " \
+               "M=8192 N=3584 K=18944 (B stored [K][N]) bf16 out"
+    elif args.workload == "wgrad":
+        d = synth.wgrad()
+        x, dy = to_dev(d["x"]), to_dev(d["dy"])
+        del d
+        T, C = x.shape
+
+        def step(timer):
+            xq, xs = timer.run("quant_col_x", lambda: mx.quantize_token(x, mx.E4M3, mx.COL_T))
+            gq, gs = timer.run("quant_col_dy", lambda: mx.quantize_token(dy, mx.E5M2, mx.COL_T))
+            timer.run("gemm", lambda: mx.block_scaled_gemm(gq, gs, mx.E5M2, xq, xs, mx.E4M3, mx.B_NK,
+                                                            mx.SCALE_ROW128))
+        sizes = {"quant_col_x": bytes_token(T, C, 2), "quant_col_dy": bytes_token(T, C, 2)}
+        M = N = C
+        K = T
+        flops = 2.0 * M * N * K
+        desc = "wgrad: column-quantize X and dY 16384x4096 bf16 along tokens (E4M3 / E5M2) + GEMM M=N=4096 " \
+               "K=16384 fp32 out"
+    else:
+        xs = [to_dev(synth.mxstress_tensor(j)) for j in range(64)]
+        R, C = xs[0].shape
+
+        def step(timer):
+            for j in range(64):
+                timer.run("mx_quant", lambda: mx.quantize_mx(xs[j], mx.E4M3, mx.RULE_FLOOR, counts=True))
+        sizes = {"mx_quant": R * C * 5 + 2 * R * (C // 32)}
+        flops = 0.0
+        M = N = K = 0
+        desc = "mxstress: 64 tensors 4096x4096 fp32, MX 32-element E4M3 blocks, OCP floor scales, clamp counts"
+    per_step, timer = time_steps(step, args.steps, args.warmup)
+    for name, b in sizes.items():
+        t = timer.mean(name)
+        kern[name] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
+                      "frac_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4), "bytes": b}
+    if flops:
+        g = timer.mean("gemm")
+        kern["gemm"] = {"us": round(g * 1e6, 2), "TFLOP/s": round(flops / g / 1e12, 1),
+                        "frac_fp8_peak": round(flops / g / 1e12 / FP8_PEAK_TFLOPS, 4), "flops": flops}
+        value, unit = flops / per_step / 1e12, "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": round(flops / g / 1e12, 2), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(flops / g / 1e12 / FP8_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        tot = sum(sizes.values()) * 64
+        value, unit = tot / per_step / 1e9, "GB/s"
+        roof = {"bound": "hbm", "achieved": kern["mx_quant"]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": kern["mx_quant"]["frac_hbm_peak"], "traffic": None}
+    return {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(per_step * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8", "data": "synthetic (seeded numpy PCG64)",
+        "config": {"workload": desc, "M": M, "N": N, "K": K}, "kernels": kern, "roofline": roof,
+        "cpu_baseline": None,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mx_block_scaled_x128_amd as mx
+    mx.load_library()  # fail loudly if the HIP library is not built
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    line = bench_fprop(args) if args.workload == "fprop1p5b" else bench_other(args)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,28 @@
+// launch.hpp -- internal host launchers behind the C ABI (argument checking
+// is done by the caller, api.cpp; these only size grids and launch).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxfp8 {
+
+// Token-wise 1x128 groups along rows.  cols % 16 == 0.
+void launch_quant_row(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                      uint8_t* q, int64_t ldq, uint8_t* s, hipStream_t stream);
+// 128-token groups down columns, transposed codes.  rows % 16 == 0, cols % 16 == 0.
+void launch_quant_col_t(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                        uint8_t* qt, int64_t ldq, uint8_t* st, hipStream_t stream);
+// 128x128 tiles.  cols % 16 == 0.
+void launch_quant_block(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw, int fmt,
+                        uint8_t* q, int64_t ldq, uint8_t* s, hipStream_t stream);
+// 32-element MX blocks along rows.  cols % 32 == 0.
+void launch_mx(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt, int rule,
+               uint8_t* q, int64_t ldq, uint8_t* s, uint8_t* counts, hipStream_t stream);
+// Block-scaled GEMM.  K % 128 == 0, M, N >= 1.
+void launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, int a_fmt,
+                 const uint8_t* sa, const uint8_t* b, int64_t ldb, int b_fmt, int b_layout,
+                 const uint8_t* sb, int b_scale_mode, void* c, int64_t ldc, int c_dtype,
+                 hipStream_t stream);
+
+}  // namespace mxfp8

@@ -1,0 +1,368 @@
+// quant.hip -- HBM-streaming FP8 quantizers for gfx950.
+//
+// Token-wise 1x128 groups (activations / gradients) and 128x128 tiles
+// (weights) with round-up power-of-two UE8M0 scales ["A Comprehensive FP8
+// Training Recipe for Reasoning-Enhanced Language Models", "What carries the
+// argument", Figs. 1-2]; 32-element MX blocks with the OCP floor rule and the
+// clamp counter ["Characterization and Mitigation of Training Instabilities in
+// Microscaling Formats", "What carries the argument", Fig. 5].
+//
+// Every kernel reads its input once (16-byte vector loads, 8 elements per
+// lane), reduces amax with DPP inside the wavefront (LDS only where a group
+// spans waves), and writes packed codes (8 bytes per lane).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace mxfp8 {
+
+namespace quant_detail {
+
+constexpr int kThreads = 256;
+constexpr uint32_t kMaxBlocks = 256 * 8;  // 8 workgroups per CU, grid-stride beyond that
+
+__device__ __forceinline__ void zero8(float (&f)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = 0.0f;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint2 codes8(const float (&f)[8], float sc) {
+  uint2 o;
+  o.x = cvt4<FMT>(f[0] * sc, f[1] * sc, f[2] * sc, f[3] * sc);
+  o.y = cvt4<FMT>(f[4] * sc, f[5] * sc, f[6] * sc, f[7] * sc);
+  return o;
+}
+
+// ---------------------------------------------------------------------------
+// 1x128 groups along rows.  A wavefront handles "items" of 4 consecutive
+// groups of one row: 16 lanes per group, 8 elements per lane.  Items are
+// wave-uniform, so the row / column split runs on the scalar unit.
+// ---------------------------------------------------------------------------
+template <typename InT, int FMT, int U>
+__global__ __launch_bounds__(kThreads) void quant_row_kernel(
+    const InT* __restrict__ x, uint32_t cols, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+    uint8_t* __restrict__ s, uint32_t ngroups, uint32_t ipr, uint32_t total_items) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t sub = lane & 15;
+  const uint32_t slot = lane >> 4;
+  const uint32_t wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const uint32_t nwaves = gridDim.x * (kThreads / 64);
+  for (uint32_t it = wave * U; it < total_items; it += nwaves * U) {
+    float f[U][8];
+    uint32_t row[U], grp[U];
+    bool act[U], gvalid[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t item = it + u;
+      const uint32_t r = item / ipr;
+      const uint32_t g = (item - r * ipr) * 4 + slot;
+      const uint32_t c = g * 128 + sub * 8;
+      row[u] = r;
+      grp[u] = g;
+      gvalid[u] = item < total_items && g < ngroups;
+      act[u] = gvalid[u] && c < cols;
+      if (act[u]) load8(x + (int64_t)r * ldx + c, f[u]);
+      else zero8(f[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = max(m, abs_bits(f[u][j]));
+      m = max_row16(m);
+      const int e = scale_exp_ceil<FMT>(m);
+      const float sc = pow2_neg(e);
+      if (act[u])
+        *reinterpret_cast<uint2*>(q + (int64_t)row[u] * ldq + grp[u] * 128 + sub * 8) = codes8<FMT>(f[u], sc);
+      if (sub == 0 && gvalid[u]) s[(int64_t)row[u] * ngroups + grp[u]] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128-token groups down columns, codes written transposed (token axis
+// contiguous).  One workgroup per 128 tokens x 128 channels tile: each thread
+// holds 8 tokens x 8 channels in registers; column maxima reduce over the 8
+// lanes of a wave that share a channel chunk (DPP), then over the two waves
+// that cover the tile's token halves (LDS).  Codes are transposed through an
+// LDS tile whose rows are padded to 136 bytes so that the 8-byte writes of a
+// wavefront fall on distinct banks.
+// ---------------------------------------------------------------------------
+constexpr int kColPitch = 136;
+
+template <typename InT, int FMT>
+__global__ __launch_bounds__(kThreads) void quant_col_t_kernel(
+    const InT* __restrict__ x, uint32_t rows, uint32_t cols, int64_t ldx, uint8_t* __restrict__ qt,
+    int64_t ldq, uint8_t* __restrict__ st, uint32_t ngt) {
+  __shared__ uint32_t red[2][128];
+  __shared__ int exps[128];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * kColPitch];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint32_t tr = (lane & 7) + 8 * (w & 1);   // token chunk: tokens tr*8 .. tr*8+7
+  const uint32_t tc = (lane >> 3) + 8 * (w >> 1); // channel chunk: channels tc*8 .. tc*8+7
+  const uint32_t c0 = blockIdx.x * 128, t0 = blockIdx.y * 128;
+  const bool cact = c0 + tc * 8 < cols;
+  float f[8][8];  // [token][channel]
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t r = t0 + tr * 8 + i;
+    if (cact && r < rows) load8(x + (int64_t)r * ldx + c0 + tc * 8, f[i]);
+    else zero8(f[i]);
+  }
+  uint32_t m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t a = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = max(a, abs_bits(f[i][j]));
+    m[j] = max_oct(a);
+  }
+  if ((lane & 7) == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[w & 1][tc * 8 + j] = m[j];
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const uint32_t a = max(red[0][tid], red[1][tid]);
+    const int e = scale_exp_ceil<FMT>(a);
+    exps[tid] = e;
+    if (c0 + tid < cols) st[(int64_t)(c0 + tid) * ngt + blockIdx.y] = (uint8_t)(e + 127);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float sc = pow2_neg(exps[tc * 8 + j]);
+    uint2 o;
+    o.x = cvt4<FMT>(f[0][j] * sc, f[1][j] * sc, f[2][j] * sc, f[3][j] * sc);
+    o.y = cvt4<FMT>(f[4][j] * sc, f[5][j] * sc, f[6][j] * sc, f[7][j] * sc);
+    *reinterpret_cast<uint2*>(tile + (tc * 8 + j) * kColPitch + tr * 8) = o;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rep = 0; rep < 4; ++rep) {
+    const uint32_t idx = rep * kThreads + tid;
+    const uint32_t ch = idx >> 3, ck = idx & 7;
+    if (c0 + ch < cols && t0 + ck * 16 < rows) {
+      const uint2 a = *reinterpret_cast<const uint2*>(tile + ch * kColPitch + ck * 16);
+      const uint2 b = *reinterpret_cast<const uint2*>(tile + ch * kColPitch + ck * 16 + 8);
+      *reinterpret_cast<uint4*>(qt + (int64_t)(c0 + ch) * ldq + t0 + ck * 16) = make_uint4(a.x, a.y, b.x, b.y);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 tiles.  One workgroup per tile, the whole tile held in registers
+// (8 rows x 8 columns per thread), amax by DPP + cross-lane shuffles inside
+// each wavefront and 4 values through LDS across wavefronts; then one pass of
+// casts and 8-byte stores.  Input is read from HBM exactly once.
+// ---------------------------------------------------------------------------
+template <typename InT, int FMT>
+__global__ __launch_bounds__(kThreads) void quant_block_kernel(
+    const InT* __restrict__ w, uint32_t rows, uint32_t cols, int64_t ldw, uint8_t* __restrict__ q,
+    int64_t ldq, uint8_t* __restrict__ s, uint32_t nbc) {
+  __shared__ uint32_t red[4];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t tc = lane & 15;               // column chunk: columns tc*8 .. tc*8+7
+  const uint32_t tr = (lane >> 4) + 4 * wv;    // row chunk: rows tr*8 .. tr*8+7
+  const uint32_t r0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
+  const bool cact = c0 + tc * 8 < cols;
+  float f[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t r = r0 + tr * 8 + i;
+    if (cact && r < rows) load8(w + (int64_t)r * ldw + c0 + tc * 8, f[i]);
+    else zero8(f[i]);
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = max(m, abs_bits(f[i][j]));
+  m = max_wave(m);
+  if (lane == 0) red[wv] = m;
+  __syncthreads();
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  const int e = scale_exp_ceil<FMT>(m);
+  const float sc = pow2_neg(e);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t r = r0 + tr * 8 + i;
+    if (cact && r < rows)
+      *reinterpret_cast<uint2*>(q + (int64_t)r * ldq + c0 + tc * 8) = codes8<FMT>(f[i], sc);
+  }
+  if (tid == 0) s[(int64_t)blockIdx.y * nbc + blockIdx.x] = (uint8_t)(e + 127);
+}
+
+// ---------------------------------------------------------------------------
+// 32-element MX blocks along rows: 4 lanes x 8 elements per block, 16 blocks
+// of one row per wavefront item.  RULE 1 = OCP floor exponent, whose scaled
+// values may exceed fmax: those are counted (optional) and clamped before the
+// cast, which is the saturation of the last bin.  RULE 0 = round-up exponent.
+// ---------------------------------------------------------------------------
+template <typename InT, int FMT, int RULE, bool COUNTS, int U>
+__global__ __launch_bounds__(kThreads) void mx_kernel(
+    const InT* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+    uint8_t* __restrict__ s, uint8_t* __restrict__ cnt, uint32_t nblk, uint32_t ipr,
+    uint32_t total_items) {
+  constexpr float fmax = FmtInfo<FMT>::fmax;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t sub = lane & 3;
+  const uint32_t slot = lane >> 2;
+  const uint32_t wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const uint32_t nwaves = gridDim.x * (kThreads / 64);
+  for (uint32_t it = wave * U; it < total_items; it += nwaves * U) {
+    float f[U][8];
+    uint32_t row[U], blk[U];
+    bool act[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t item = it + u;
+      const uint32_t r = item / ipr;
+      const uint32_t b = (item - r * ipr) * 16 + slot;
+      row[u] = r;
+      blk[u] = b;
+      act[u] = item < total_items && b < nblk;
+      if (act[u]) load8(x + (int64_t)r * ldx + b * 32 + sub * 8, f[u]);
+      else zero8(f[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = max(m, abs_bits(f[u][j]));
+      m = max_quad(m);
+      const int e = RULE == 1 ? scale_exp_floor<FMT>(m) : scale_exp_ceil<FMT>(m);
+      const float sc = pow2_neg(e);
+      float v[8];
+      uint32_t n = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        v[j] = f[u][j] * sc;
+        if (COUNTS) n += fabsf(v[j]) > fmax ? 1u : 0u;
+        v[j] = __builtin_amdgcn_fmed3f(v[j], -fmax, fmax);
+      }
+      if (COUNTS) n = sum_quad(n);
+      if (act[u]) {
+        uint2 o;
+        o.x = cvt4<FMT>(v[0], v[1], v[2], v[3]);
+        o.y = cvt4<FMT>(v[4], v[5], v[6], v[7]);
+        *reinterpret_cast<uint2*>(q + (int64_t)row[u] * ldq + blk[u] * 32 + sub * 8) = o;
+        if (sub == 0) {
+          s[(int64_t)row[u] * nblk + blk[u]] = (uint8_t)(e + 127);
+          if (COUNTS) cnt[(int64_t)row[u] * nblk + blk[u]] = (uint8_t)n;
+        }
+      }
+    }
+  }
+}
+
+uint32_t grid_for(uint64_t items, int per_wave) {
+  const uint64_t waves = (items + per_wave - 1) / per_wave;
+  uint64_t blocks = (waves + 3) / 4;
+  if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+  return blocks ? (uint32_t)blocks : 1u;
+}
+
+}  // namespace quant_detail
+
+using namespace quant_detail;
+
+// ----------------------------------------------------------------- launchers
+
+template <typename InT, int FMT>
+static void row_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* q,
+                         int64_t ldq, uint8_t* s, hipStream_t st) {
+  constexpr int U = 2;
+  const uint32_t ngroups = (uint32_t)((cols + 127) / 128);
+  const uint32_t ipr = (ngroups + 3) / 4;
+  const uint64_t items = (uint64_t)rows * ipr;
+  hipLaunchKernelGGL((quant_row_kernel<InT, FMT, U>), dim3(grid_for(items, U)), dim3(kThreads), 0, st,
+                     (const InT*)x, (uint32_t)cols, ldx, q, ldq, s, ngroups, ipr, (uint32_t)items);
+}
+
+void launch_quant_row(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                      uint8_t* q, int64_t ldq, uint8_t* s, hipStream_t st) {
+  if (dtype == 1) {
+    if (fmt == 0) row_dispatch<uint16_t, 0>(x, rows, cols, ldx, q, ldq, s, st);
+    else row_dispatch<uint16_t, 1>(x, rows, cols, ldx, q, ldq, s, st);
+  } else {
+    if (fmt == 0) row_dispatch<float, 0>(x, rows, cols, ldx, q, ldq, s, st);
+    else row_dispatch<float, 1>(x, rows, cols, ldx, q, ldq, s, st);
+  }
+}
+
+template <typename InT, int FMT>
+static void col_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* qt,
+                         int64_t ldq, uint8_t* st, hipStream_t stream) {
+  const uint32_t ngt = (uint32_t)((rows + 127) / 128);
+  const dim3 grid((uint32_t)((cols + 127) / 128), ngt);
+  hipLaunchKernelGGL((quant_col_t_kernel<InT, FMT>), grid, dim3(kThreads), 0, stream, (const InT*)x,
+                     (uint32_t)rows, (uint32_t)cols, ldx, qt, ldq, st, ngt);
+}
+
+void launch_quant_col_t(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                        uint8_t* qt, int64_t ldq, uint8_t* st, hipStream_t stream) {
+  if (dtype == 1) {
+    if (fmt == 0) col_dispatch<uint16_t, 0>(x, rows, cols, ldx, qt, ldq, st, stream);
+    else col_dispatch<uint16_t, 1>(x, rows, cols, ldx, qt, ldq, st, stream);
+  } else {
+    if (fmt == 0) col_dispatch<float, 0>(x, rows, cols, ldx, qt, ldq, st, stream);
+    else col_dispatch<float, 1>(x, rows, cols, ldx, qt, ldq, st, stream);
+  }
+}
+
+template <typename InT, int FMT>
+static void block_dispatch(const void* w, int64_t rows, int64_t cols, int64_t ldw, uint8_t* q,
+                           int64_t ldq, uint8_t* s, hipStream_t stream) {
+  const uint32_t nbc = (uint32_t)((cols + 127) / 128);
+  const dim3 grid(nbc, (uint32_t)((rows + 127) / 128));
+  hipLaunchKernelGGL((quant_block_kernel<InT, FMT>), grid, dim3(kThreads), 0, stream, (const InT*)w,
+                     (uint32_t)rows, (uint32_t)cols, ldw, q, ldq, s, nbc);
+}
+
+void launch_quant_block(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw, int fmt,
+                        uint8_t* q, int64_t ldq, uint8_t* s, hipStream_t stream) {
+  if (dtype == 1) {
+    if (fmt == 0) block_dispatch<uint16_t, 0>(w, rows, cols, ldw, q, ldq, s, stream);
+    else block_dispatch<uint16_t, 1>(w, rows, cols, ldw, q, ldq, s, stream);
+  } else {
+    if (fmt == 0) block_dispatch<float, 0>(w, rows, cols, ldw, q, ldq, s, stream);
+    else block_dispatch<float, 1>(w, rows, cols, ldw, q, ldq, s, stream);
+  }
+}
+
+template <typename InT, int FMT, int RULE, bool COUNTS>
+static void mx_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
+                        uint8_t* s, uint8_t* counts, hipStream_t stream) {
+  constexpr int U = 2;
+  const uint32_t nblk = (uint32_t)(cols / 32);
+  const uint32_t ipr = (nblk + 15) / 16;
+  const uint64_t items = (uint64_t)rows * ipr;
+  hipLaunchKernelGGL((mx_kernel<InT, FMT, RULE, COUNTS, U>), dim3(grid_for(items, U)), dim3(kThreads), 0,
+                     stream, (const InT*)x, ldx, q, ldq, s, counts, nblk, ipr, (uint32_t)items);
+}
+
+template <typename InT, int FMT>
+static void mx_dispatch_rule(const void* x, int64_t rows, int64_t cols, int64_t ldx, int rule, uint8_t* q,
+                             int64_t ldq, uint8_t* s, uint8_t* counts, hipStream_t stream) {
+  if (rule == 1) {
+    if (counts) mx_dispatch<InT, FMT, 1, true>(x, rows, cols, ldx, q, ldq, s, counts, stream);
+    else mx_dispatch<InT, FMT, 1, false>(x, rows, cols, ldx, q, ldq, s, counts, stream);
+  } else {
+    if (counts) mx_dispatch<InT, FMT, 0, true>(x, rows, cols, ldx, q, ldq, s, counts, stream);
+    else mx_dispatch<InT, FMT, 0, false>(x, rows, cols, ldx, q, ldq, s, counts, stream);
+  }
+}
+
+void launch_mx(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt, int rule,
+               uint8_t* q, int64_t ldq, uint8_t* s, uint8_t* counts, hipStream_t stream) {
+  if (dtype == 1) {
+    if (fmt == 0) mx_dispatch_rule<uint16_t, 0>(x, rows, cols, ldx, rule, q, ldq, s, counts, stream);
+    else mx_dispatch_rule<uint16_t, 1>(x, rows, cols, ldx, rule, q, ldq, s, counts, stream);
+  } else {
+    if (fmt == 0) mx_dispatch_rule<float, 0>(x, rows, cols, ldx, rule, q, ldq, s, counts, stream);
+    else mx_dispatch_rule<float, 1>(x, rows, cols, ldx, rule, q, ldq, s, counts, stream);
+  }
+}
+
+}  // namespace mxfp8

@@ -28,3 +28,12 @@ def read_golden(name):
 @pytest.fixture(scope="session")
 def golden():
     return read_golden
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Print the case name (flushed, uncaptured) before every GPU test runs."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write("\n[gpu case] %s\n" % request.node.nodeid)
+        sys.__stderr__.flush()
+    yield

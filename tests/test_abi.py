@@ -1,0 +1,112 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function that
+include/mxfp8.h declares, and rejects every invalid argument with the documented
+status before any HIP call (fake, never-dereferenced pointers)."""
+import os
+import re
+
+import pytest
+
+import mx_block_scaled_x128_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp8.h")
+
+OK, NULL, SHAPE, LD, ALIGN, ENUM, ALIAS = 0, 1, 2, 3, 4, 5, 6
+X, Q, S, C, P2 = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000  # fake aligned device pointers
+MIS = 0x200008  # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = mx.load_library()
+    names = declared_functions()
+    assert set(names) >= {"fp8_quantize_token", "fp8_quantize_block", "mx_quantize", "fp8_block_scaled_gemm",
+                          "mxfp8_status_string", "mxfp8_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert mx.mxfp8_version() == 100
+    for st in range(8):
+        assert mx.mxfp8_status_string(st)
+    assert mx.mxfp8_status_string(99) == "unknown status"
+
+
+def tok(x=X, dt=1, rows=256, cols=512, ldx=512, axis=0, fmt=0, q=Q, ldq=512, s=S):
+    return mx.fp8_quantize_token(x, dt, rows, cols, ldx, axis, fmt, q, ldq, s, None)
+
+
+def test_token_validation():
+    assert tok(dt=2) == ENUM
+    assert tok(axis=2) == ENUM
+    assert tok(fmt=7) == ENUM
+    assert tok(rows=-1) == SHAPE
+    assert tok(rows=0) == OK and tok(cols=0, x=None, q=None, s=None) == OK  # empty: no launch
+    assert tok(x=None) == NULL and tok(q=None) == NULL and tok(s=None) == NULL
+    assert tok(ldx=500) == LD and tok(ldx=520) == LD and tok(ldq=500) == LD
+    assert tok(cols=520, ldx=528, ldq=528) == SHAPE  # cols % 16
+    assert tok(x=MIS) == ALIGN and tok(q=MIS) == ALIGN
+    assert tok(q=X) == ALIAS and tok(s=X) == ALIAS and tok(s=Q) == ALIAS
+    # COL_T: q is [cols][rows]; rows must be a multiple of 16
+    assert tok(axis=1, rows=256, cols=512, ldx=512, ldq=240) == LD
+    assert tok(axis=1, rows=136, cols=512, ldx=512, ldq=144) == SHAPE
+    assert tok(rows=2 ** 31, ldx=512) == SHAPE
+
+
+def blk(w=X, dt=0, rows=256, cols=512, ldw=512, fmt=1, q=Q, ldq=512, s=S):
+    return mx.fp8_quantize_block(w, dt, rows, cols, ldw, fmt, q, ldq, s, None)
+
+
+def test_block_validation():
+    assert blk(dt=-1) == ENUM and blk(fmt=2) == ENUM
+    assert blk(cols=-16) == SHAPE and blk(cols=24, ldw=32, ldq=32) == SHAPE
+    assert blk(rows=0, w=None) == OK
+    assert blk(w=None) == NULL
+    assert blk(ldw=16) == LD and blk(ldq=520) == LD
+    assert blk(w=MIS) == ALIGN
+    assert blk(q=X) == ALIAS
+
+
+def mxq(x=X, dt=0, rows=64, cols=256, ldx=256, fmt=0, rule=1, q=Q, ldq=256, s=S, cnt=P2):
+    return mx.mx_quantize(x, dt, rows, cols, ldx, fmt, rule, q, ldq, s, cnt, None)
+
+
+def test_mx_validation():
+    assert mxq(rule=2) == ENUM and mxq(fmt=3) == ENUM and mxq(dt=5) == ENUM
+    assert mxq(cols=48, ldx=48, ldq=48) == SHAPE
+    assert mxq(s=None) == NULL
+    assert mxq(ldq=255) == LD
+    assert mxq(cnt=X) == ALIAS and mxq(cnt=Q) == ALIAS and mxq(cnt=S) == ALIAS
+    assert mxq(x=MIS) == ALIGN
+    assert mxq(rows=0) == OK
+
+
+def gemm(M=256, N=256, K=512, a=X, lda=512, afmt=0, sa=S, b=Q, ldb=512, bfmt=0, blay=0, sb=P2, bsm=0, c=C,
+         ldc=256, cdt=0):
+    return mx.fp8_block_scaled_gemm(M, N, K, a, lda, afmt, sa, b, ldb, bfmt, blay, sb, bsm, c, ldc, cdt, None)
+
+
+def test_gemm_validation():
+    assert gemm(afmt=2) == ENUM and gemm(bfmt=-1) == ENUM and gemm(blay=2) == ENUM
+    assert gemm(bsm=2) == ENUM and gemm(cdt=3) == ENUM
+    assert gemm(blay=1, bsm=1, ldb=256) == ENUM  # per-row B scales only with [N][K] storage
+    assert gemm(K=500) == SHAPE and gemm(M=-1) == SHAPE
+    assert gemm(M=0) == OK and gemm(N=0, c=None) == OK
+    assert gemm(c=None) == NULL and gemm(a=None) == NULL and gemm(sb=None) == NULL
+    assert gemm(lda=256) == LD and gemm(ldb=500) == LD and gemm(ldc=200) == LD
+    assert gemm(blay=1, ldb=128) == LD  # KN: ldb >= N
+    assert gemm(a=MIS) == ALIGN and gemm(c=MIS) == ALIGN
+    assert gemm(c=X) == ALIAS and gemm(c=S) == ALIAS
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(mx, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(mx, "_lib", None)
+    with pytest.raises(ImportError):
+        mx.load_library()

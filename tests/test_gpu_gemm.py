@@ -1,0 +1,130 @@
+"""GPU parity of the block-scaled FP8 GEMM against the CPU oracle (fp64 over
+dequantized operands), through the C ABI.  Bound per element:
+|y_gpu - y| <= 2^-12 * sum_k |a*b| (+ one bf16 rounding for bf16 output)."""
+import numpy as np
+import pytest
+import torch
+
+import mx_block_scaled_x128_amd as mx
+import oracle
+import synth
+from gpu_helpers import assert_gemm_close, dev, host, run_gemm
+
+pytestmark = pytest.mark.gpu
+
+FMT_PAIRS = [(0, 0), (1, 0), (0, 1), (1, 1)]
+
+
+def finite_codes(fmt):
+    vals = oracle.decode(fmt, np.arange(256, dtype=np.uint8))
+    return np.array([c for c in range(256) if np.isfinite(vals[c])], dtype=np.uint8)
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", FMT_PAIRS)
+@pytest.mark.parametrize("b_layout", [mx.B_NK, mx.B_KN])
+def test_outer_products_of_every_code_pair_exact(a_fmt, b_fmt, b_layout):
+    """C[i][j] = dec(a_i) * dec(b_j) exactly (an 8-bit significand product fits fp32):
+    pins the operand formats, subnormal handling and the output layout."""
+    ca, cb = finite_codes(a_fmt), finite_codes(b_fmt)
+    M, N, K = len(ca), len(cb), 256
+    a = np.zeros((M, K), np.uint8)
+    b_nk = np.zeros((N, K), np.uint8)
+    a[:, 131] = ca  # second K block, inside the block
+    b_nk[:, 131] = cb
+    sa = np.full((M, 2), 127, np.uint8)
+    if b_layout == mx.B_NK:
+        b, sb = b_nk, np.full((-(-N // 128), 2), 127, np.uint8)
+    else:
+        b, sb = np.ascontiguousarray(b_nk.T), np.full((2, -(-N // 128)), 127, np.uint8)
+    y = run_gemm(a, sa, a_fmt, b, sb, b_fmt, b_layout, mx.SCALE_BLOCK128, False)
+    ref = np.outer(oracle.decode(a_fmt, ca), oracle.decode(b_fmt, cb))
+    assert np.array_equal(y.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("b_layout,b_scale", [(mx.B_NK, mx.SCALE_BLOCK128), (mx.B_KN, mx.SCALE_BLOCK128),
+                                              (mx.B_NK, mx.SCALE_ROW128)])
+def test_each_scale_byte_moves_only_its_block(b_layout, b_scale):
+    M, N, K = 256, 256, 512
+    a = synth.random_codes(1, (M, K), 0)
+    b_nk = synth.random_codes(2, (N, K), 0)
+    sa = np.full((M, K // 128), 127, np.uint8)
+    sa[5, 2] = 130  # row 5, K block 2 scaled by 8
+    if b_scale == mx.SCALE_ROW128:
+        sb = np.full((N, K // 128), 127, np.uint8)
+        sb[200, 1] = 125
+    else:
+        sb = np.full((2, K // 128), 127, np.uint8)
+        sb[1, 3] = 129
+    b = b_nk if b_layout == mx.B_NK else np.ascontiguousarray(b_nk.T)
+    sb_store = sb if b_layout == mx.B_NK else np.ascontiguousarray(sb.T)
+    y = run_gemm(a, sa, 0, b, sb_store, 0, b_layout, b_scale, False)
+    y_ref, t_ref = oracle.gemm(a, sa, 0, b, sb_store, 0, b_layout, b_scale)
+    assert_gemm_close(y, y_ref, t_ref, False, "scale bump")
+
+
+SHAPES = [(1, 16, 128), (77, 130, 384), (256 + 40, 384 + 24, 1024), (128, 128, 128 * 12), (513, 257, 256)]
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", FMT_PAIRS)
+@pytest.mark.parametrize("b_layout,b_scale", [(mx.B_NK, mx.SCALE_BLOCK128), (mx.B_KN, mx.SCALE_BLOCK128),
+                                              (mx.B_NK, mx.SCALE_ROW128)])
+@pytest.mark.parametrize("bf16_out", [False, True])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_random_codes_parity(a_fmt, b_fmt, b_layout, b_scale, bf16_out, shape):
+    M, N, K = shape
+    seed = M * 31 + N * 7 + K + 100 * a_fmt + 10 * b_fmt
+    a = synth.random_codes(seed, (M, K), a_fmt)
+    b_nk = synth.random_codes(seed + 1, (N, K), b_fmt)
+    sa = synth.random_scale_bytes(seed + 2, (M, K // 128))
+    if b_scale == mx.SCALE_ROW128:
+        sb = synth.random_scale_bytes(seed + 3, (N, K // 128))
+    else:
+        sb = synth.random_scale_bytes(seed + 3, (-(-N // 128), K // 128))
+    b = b_nk if b_layout == mx.B_NK else np.ascontiguousarray(b_nk.T)
+    sb_store = sb if (b_layout == mx.B_NK) else np.ascontiguousarray(sb.T)
+    y = run_gemm(a, sa, a_fmt, b, sb_store, b_fmt, b_layout, b_scale, bf16_out)
+    y_ref, t_ref = oracle.gemm(a, sa, a_fmt, b, sb_store, b_fmt, b_layout, b_scale, threads=8)
+    assert_gemm_close(y, y_ref, t_ref, bf16_out, "random codes %s" % (shape,))
+
+
+def test_k_zero_writes_zeros():
+    c = torch.full((64, 48), 7.0, dtype=torch.float32, device="cuda")
+    st = mx.fp8_block_scaled_gemm(64, 48, 0, 0, 0, 0, 0, 0, 0, 0, mx.B_NK, 0, mx.SCALE_BLOCK128, c.data_ptr(),
+                                  48, mx.F32, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(c).item() == 0
+
+
+def test_ldc_larger_than_n_leaves_padding():
+    M, N, K = 100, 200, 256
+    a = synth.random_codes(5, (M, K), 0)
+    b = synth.random_codes(6, (N, K), 0)
+    sa = synth.random_scale_bytes(7, (M, 2))
+    sb = synth.random_scale_bytes(8, (2, 2))
+    c = torch.full((M, 256), -1.0, dtype=torch.float32, device="cuda")
+    ad, bd, sad, sbd = dev(a), dev(b), dev(sa), dev(sb)
+    st = mx.fp8_block_scaled_gemm(M, N, K, ad.data_ptr(), K, 0, sad.data_ptr(), bd.data_ptr(), K, 0, mx.B_NK,
+                                  sbd.data_ptr(), mx.SCALE_BLOCK128, c.data_ptr(), 256, mx.F32,
+                                  torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    ch = host(c)
+    y_ref, t_ref = oracle.gemm(a, sa, 0, b, sb, 0)
+    assert_gemm_close(ch[:, :N], y_ref, t_ref, False, "ldc")
+    assert np.all(ch[:, N:] == -1.0)
+
+
+def test_end_to_end_quantize_then_gemm_small():
+    """Quantize on the GPU (bit-exact with the oracle), then the GEMM on those bytes."""
+    d = synth.tiny()
+    xq, xs = mx.quantize_token(dev(d["x"]), mx.E4M3, mx.ROW)
+    wq, ws = mx.quantize_block(dev(d["w"]), mx.E4M3)
+    y = mx.block_scaled_gemm(xq, xs, mx.E4M3, wq, ws, mx.E4M3, mx.B_NK, mx.SCALE_BLOCK128)
+    torch.cuda.synchronize()
+    xq_ref, xs_ref = oracle.quantize_rows(d["x"], oracle.E4M3)
+    wq_ref, ws_ref = oracle.quantize_block(d["w"], oracle.E4M3)
+    assert np.array_equal(host(xq), xq_ref) and np.array_equal(host(xs), xs_ref)
+    assert np.array_equal(host(wq), wq_ref) and np.array_equal(host(ws), ws_ref)
+    y_ref, t_ref = oracle.gemm(xq_ref, xs_ref, oracle.E4M3, wq_ref, ws_ref, oracle.E4M3)
+    assert_gemm_close(host(y), y_ref, t_ref, False, "tiny end to end")
