@@ -34,9 +34,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="fprop1p5b", choices=["fprop1p5b", "dgrad7b", "wgrad", "mxstress"])
+    p.add_argument("--workload", default="fprop1p5b",
+                   choices=["fprop1p5b", "dgrad7b", "wgrad", "mxstress", "copy"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--cpu-rows", type=int, default=256, help="token rows in the oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=0,
+                   help="token rows in the oracle sample (0 = all rows: the full step)")
     return p.parse_args()
 
 
@@ -98,15 +100,37 @@ def fprop_setup():
     return {"x": to_dev(d["x"]), "w": to_dev(d["w"]), "host": d}
 
 
+def _check(st, what):
+    if st != 0:
+        raise RuntimeError("%s returned status %d" % (what, st))
+
+
 def fprop_step_fn(t):
+    """The step through the C-ABI entry points with outputs allocated once, so the events
+    bracket exactly one kernel launch each."""
     import torch
     import mx_block_scaled_x128_amd as mx
+    x, w = t["x"], t["w"]
+    M, K = x.shape
+    N = w.shape[0]
+    dev = x.device
+    xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    xs = torch.empty((M, K // 128), dtype=torch.uint8, device=dev)
+    wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    ws = torch.empty((N // 128, K // 128), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
 
     def step(timer):
-        xq, xs = timer.run("quant_token_x", lambda: mx.quantize_token(t["x"], mx.E4M3, mx.ROW))
-        wq, ws = timer.run("quant_block_w", lambda: mx.quantize_block(t["w"], mx.E4M3))
-        timer.run("gemm", lambda: mx.block_scaled_gemm(xq, xs, mx.E4M3, wq, ws, mx.E4M3, mx.B_NK,
-                                                        mx.SCALE_BLOCK128, out_dtype=torch.bfloat16))
+        _check(timer.run("quant_token_x", lambda: mx.fp8_quantize_token(
+            x.data_ptr(), mx.BF16, M, K, K, mx.ROW, mx.E4M3, xq.data_ptr(), K, xs.data_ptr(), stream)),
+            "fp8_quantize_token")
+        _check(timer.run("quant_block_w", lambda: mx.fp8_quantize_block(
+            w.data_ptr(), mx.BF16, N, K, K, mx.E4M3, wq.data_ptr(), K, ws.data_ptr(), stream)),
+            "fp8_quantize_block")
+        _check(timer.run("gemm", lambda: mx.fp8_block_scaled_gemm(
+            M, N, K, xq.data_ptr(), K, mx.E4M3, xs.data_ptr(), wq.data_ptr(), K, mx.E4M3, mx.B_NK,
+            ws.data_ptr(), mx.SCALE_BLOCK128, y.data_ptr(), N, mx.BF16, stream)), "fp8_block_scaled_gemm")
     return step
 
 
@@ -118,6 +142,7 @@ def cpu_baseline_fprop(host, rows):
     x, w = host["x"], host["w"]
     M, K = x.shape
     N = w.shape[0]
+    rows = M if rows <= 0 else min(rows, M)
     xs = np.ascontiguousarray(x[:rows])
     t0 = time.perf_counter()
     xq, xsc = oracle.quantize_rows(xs, oracle.E4M3, threads=threads)
@@ -131,9 +156,10 @@ def cpu_baseline_fprop(host, rows):
     return {
         "value": round(2.0 * M * N * K / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
         "kind": "oracle",
-        "sample": "%d of %d token rows through token quantization and the GEMM (fp64), full weight "
-                  "quantization; times scaled to the full step (%.1f s measured, %.1f s est. per step)"
-                  % (rows, M, t3 - t0, t_step),
+        "sample": ("the full step" if rows == M else
+                   "%d of %d token rows through token quantization and the GEMM, full weight quantization, "
+                   "times scaled to the full step" % (rows, M))
+                  + " (oracle: fp64 C, %d host threads; %.1f s measured, %.1f s per step)" % (threads, t3 - t0, t_step),
     }
 
 
@@ -182,11 +208,30 @@ def bench_fprop(args):
     return line
 
 
+def bench_copy(args):
+    """A plain device copy of 256 MiB (torch's copy kernel): the reference point that scales
+    profiler byte counters (FETCH_SIZE / WRITE_SIZE) to bytes, and a measured bandwidth."""
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    per_step, timer = time_steps(lambda timer: timer.run("copy", lambda: dst.copy_(src)), args.steps, args.warmup)
+    t = timer.mean("copy")
+    return {"metric": "device copy GB/s (read + write)", "value": round(2 * n / t / 1e9, 1), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(per_step * 1e3, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "copy 256 MiB", "bytes_read": n, "bytes_written": n}, "roofline": None,
+            "cpu_baseline": None}
+
+
 def bench_other(args):
-    """Per-kernel figures for the larger workloads (same JSON shape, kernels block filled)."""
+    """Per-kernel figures for the larger workloads (same JSON shape, kernels block filled).
+    Outputs are allocated once; events bracket one C-ABI launch each."""
     import torch
     import mx_block_scaled_x128_amd as mx
     import synth
+    stream = torch.cuda.current_stream().cuda_stream
+    u8 = dict(dtype=torch.uint8, device="cuda")
     kern = {}
     if args.workload == "dgrad7b":
         d = synth.dgrad7b()
@@ -194,12 +239,18 @@ def bench_other(args):
         del d
         M, K = dy.shape
         N = w.shape[1]
+        gq, gs = torch.empty((M, K), **u8), torch.empty((M, K // 128), **u8)
+        wq, ws = torch.empty((K, N), **u8), torch.empty((K // 128, N // 128), **u8)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
 
         def step(timer):
-            gq, gs = timer.run("quant_token_dy", lambda: mx.quantize_token(dy, mx.E5M2, mx.ROW))
-            wq, ws = timer.run("quant_block_w", lambda: mx.quantize_block(w, mx.E4M3))
-            timer.run("gemm", lambda: mx.block_scaled_gemm(gq, gs, mx.E5M2, wq, ws, mx.E4M3, mx.B_KN,
-                                                            mx.SCALE_BLOCK128, out_dtype=torch.bfloat16))
+            _check(timer.run("quant_token_dy", lambda: mx.fp8_quantize_token(
+                dy.data_ptr(), mx.BF16, M, K, K, mx.ROW, mx.E5M2, gq.data_ptr(), K, gs.data_ptr(), stream)), "q")
+            _check(timer.run("quant_block_w", lambda: mx.fp8_quantize_block(
+                w.data_ptr(), mx.BF16, K, N, N, mx.E4M3, wq.data_ptr(), N, ws.data_ptr(), stream)), "q")
+            _check(timer.run("gemm", lambda: mx.fp8_block_scaled_gemm(
+                M, N, K, gq.data_ptr(), K, mx.E5M2, gs.data_ptr(), wq.data_ptr(), N, mx.E4M3, mx.B_KN,
+                ws.data_ptr(), mx.SCALE_BLOCK128, y.data_ptr(), N, mx.BF16, stream)), "gemm")
         sizes = {"quant_token_dy": bytes_token(M, K, 2), "quant_block_w": bytes_block(K, N, 2)}
         flops = 2.0 * M * N * K
         desc = "dgrad7b: token-quantize dY 8192x18944 bf16 (E5M2) + block-quantize W 18944x3584 (E4M3) + GEMM " \
@@ -209,12 +260,18 @@ def bench_other(args):
         x, dy = to_dev(d["x"]), to_dev(d["dy"])
         del d
         T, C = x.shape
+        xq, xs = torch.empty((C, T), **u8), torch.empty((C, T // 128), **u8)
+        gq, gs = torch.empty((C, T), **u8), torch.empty((C, T // 128), **u8)
+        y = torch.empty((C, C), dtype=torch.float32, device="cuda")
 
         def step(timer):
-            xq, xs = timer.run("quant_col_x", lambda: mx.quantize_token(x, mx.E4M3, mx.COL_T))
-            gq, gs = timer.run("quant_col_dy", lambda: mx.quantize_token(dy, mx.E5M2, mx.COL_T))
-            timer.run("gemm", lambda: mx.block_scaled_gemm(gq, gs, mx.E5M2, xq, xs, mx.E4M3, mx.B_NK,
-                                                            mx.SCALE_ROW128))
+            _check(timer.run("quant_col_x", lambda: mx.fp8_quantize_token(
+                x.data_ptr(), mx.BF16, T, C, C, mx.COL_T, mx.E4M3, xq.data_ptr(), T, xs.data_ptr(), stream)), "q")
+            _check(timer.run("quant_col_dy", lambda: mx.fp8_quantize_token(
+                dy.data_ptr(), mx.BF16, T, C, C, mx.COL_T, mx.E5M2, gq.data_ptr(), T, gs.data_ptr(), stream)), "q")
+            _check(timer.run("gemm", lambda: mx.fp8_block_scaled_gemm(
+                C, C, T, gq.data_ptr(), T, mx.E5M2, gs.data_ptr(), xq.data_ptr(), T, mx.E4M3, mx.B_NK,
+                xs.data_ptr(), mx.SCALE_ROW128, y.data_ptr(), C, mx.F32, stream)), "gemm")
         sizes = {"quant_col_x": bytes_token(T, C, 2), "quant_col_dy": bytes_token(T, C, 2)}
         M = N = C
         K = T
@@ -222,12 +279,15 @@ def bench_other(args):
         desc = "wgrad: column-quantize X and dY 16384x4096 bf16 along tokens (E4M3 / E5M2) + GEMM M=N=4096 " \
                "K=16384 fp32 out"
     else:
-        xs = [to_dev(synth.mxstress_tensor(j)) for j in range(64)]
-        R, C = xs[0].shape
+        xs_ = [to_dev(synth.mxstress_tensor(j)) for j in range(64)]
+        R, C = xs_[0].shape
+        q, sc, cn = torch.empty((R, C), **u8), torch.empty((R, C // 32), **u8), torch.empty((R, C // 32), **u8)
 
         def step(timer):
             for j in range(64):
-                timer.run("mx_quant", lambda: mx.quantize_mx(xs[j], mx.E4M3, mx.RULE_FLOOR, counts=True))
+                _check(timer.run("mx_quant", lambda: mx.mx_quantize(
+                    xs_[j].data_ptr(), mx.F32, R, C, C, mx.E4M3, mx.RULE_FLOOR, q.data_ptr(), C, sc.data_ptr(),
+                    cn.data_ptr(), stream)), "mx")
         sizes = {"mx_quant": R * C * 5 + 2 * R * (C // 32)}
         flops = 0.0
         M = N = K = 0
@@ -270,7 +330,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    line = bench_fprop(args) if args.workload == "fprop1p5b" else bench_other(args)
+    if args.workload == "fprop1p5b":
+        line = bench_fprop(args)
+    elif args.workload == "copy":
+        line = bench_copy(args)
+    else:
+        line = bench_other(args)
     print(json.dumps(line), flush=True)
 
 

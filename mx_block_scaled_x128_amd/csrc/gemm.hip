@@ -8,26 +8,30 @@
 // argument"].
 //
 // Design (gfx950 specifics):
-//  * One v_mfma_scale_f32_16x16x128_f8f6f4 covers exactly one 128-wide K
-//    block.  Its E8M0 scale operands take the per-row A scale and the per-
-//    column B scale of that block, so the per-block rescale happens inside the
-//    matrix core and every K block accumulates straight into the fp32
-//    accumulators (no separate partial-sum rescale).  The MFMA multiplies
-//    products exactly and adds at most K/128 block results per output into
-//    fp32, which keeps the error far below 2^-12 * sum|a*b|.
-//  * Operands are swapped (B fragment first) so that each lane owns 4
+//  * v_mfma_scale_f32_32x32x64_f8f6f4 applies per-row E8M0 scales of both
+//    operands inside the matrix core; two of them (two 64-wide K stages)
+//    cover one 128-wide scale block with the same scale bytes.  Every block's
+//    partial product therefore accumulates directly into the fp32
+//    accumulators: no separate per-block rescale pass.  Products of FP8
+//    values are exact; fp32 accumulation over 64-term MFMA sums keeps the
+//    error far below 2^-12 * sum|a*b|.
+//  * Operands are swapped (B fragment first), so each lane owns runs of 4
 //    consecutive output columns of one row: 16-byte (fp32) / 8-byte (bf16)
 //    stores.
-//  * Tiles move HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging),
-//    double buffered: the loads for K block ks+1 are in flight while the
-//    MFMAs of block ks run.  Rows of the [rows][128 B] LDS tiles are XOR-
-//    swizzled in 16-byte chunks so that fragment reads (two ds_read_b128 per
-//    lane) are bank-conflict free.
-//  * B stored [K][N] (the dgrad case): the tile is kept as [128 k][BN bytes]
-//    and read with ds_read_b64_tr_b8, which transposes 8x16-byte blocks across
-//    a 16-lane group, giving each lane 8 consecutive k of one column.
-//  * Workgroup ids are remapped so that each XCD (8 per device, own L2) walks
-//    a contiguous band of tiles in grouped-row order.
+//  * HBM -> LDS moves use global_load_lds_dwordx4 (no VGPR staging) into a
+//    ring of STAGES buffers, STAGES stages ahead of the MFMAs.  Fragments are
+//    double-buffered in registers: the next stage's ds_reads are interleaved
+//    into the current stage's MFMA stream.  One barrier per 64-wide stage.
+//  * Rows of the [rows][64 B] LDS tiles are XOR-swizzled in 16-byte chunks so
+//    fragment reads (two ds_read_b128 per lane) are bank-conflict free.
+//  * B stored [K][N] (the data-gradient case): the stage tile is kept as
+//    [64 k][BN bytes] and read with ds_read_b64_tr_b8, which transposes an
+//    8 x 16-byte block across a 16-lane group and hands each lane 8
+//    consecutive k of one column.
+//  * Workgroup ids are remapped so each XCD (8 per device, own L2) walks a
+//    contiguous band of tiles in grouped-row order.
+//  * Source addresses are a wave-uniform (SGPR) tile base plus 32-bit per-lane
+//    offsets, so the address registers do not compete with the fragments.
 #include "launch.hpp"
 
 #include <stdint.h>
@@ -40,10 +44,12 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
 constexpr int kThreads = 256;  // 4 waves, arranged 2 x 2 over the tile
+constexpr int BK = 64;         // K per pipeline stage
 
 __device__ __forceinline__ uint32_t bf16_rne(float v) {
   uint32_t b = __float_as_uint(v);
@@ -51,69 +57,61 @@ __device__ __forceinline__ uint32_t bf16_rne(float v) {
   return b >> 16;
 }
 
-// 16-byte chunk swizzle of the [rows][128 B] tiles: row r, logical chunk c
-// lives at physical chunk c ^ ((r >> 1) & 7).  Sixteen consecutive rows read
-// at one logical chunk then cover all 64 banks exactly once.
-__device__ __forceinline__ uint32_t swz_rows(uint32_t r) { return (r >> 1) & 7; }
+// [rows][64 B] stage tiles: row r, logical 16-byte chunk c at physical chunk
+// c ^ ((r >> 2) & 3); sixteen consecutive rows read at one logical chunk hit
+// 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
 
-// Swizzle of the [128 k][BN bytes] tile for B stored [K][N]; CPR = BN / 16
-// chunks per row.  The eight rows that one transposed read touches land on
-// distinct chunks, and the two 16-lane halves of a wave use disjoint halves of
-// the row when CPR == 16.
+// [64 k][BN bytes] stage tiles of B stored [K][N] (CPR = BN / 16 chunks per
+// row): chunk c of row k at physical chunk c ^ s(k), s(k) even, so the two
+// 16-column halves of a 32-column fragment (chunks 2p, 2p+1) and the eight
+// rows of one transposed read cover 16 distinct bank groups.
 template <int CPR>
-__device__ __forceinline__ uint32_t swz_kn(uint32_t k) {
-  return CPR == 16 ? ((k & 7) | (((k >> 5) & 1) << 3)) : (k & 7);
+__device__ __forceinline__ int swz_kn(int k) {
+  return CPR == 16 ? 2 * (k & 7) : 2 * ((k >> 1) & 3);
 }
 
-// HBM -> LDS for one K block: each wave-instruction moves 1 KB (64 lanes x 16
-// bytes) to consecutive LDS; the per-lane source addresses encode the swizzle.
-template <int A_LOADS, int B_LOADS>
-__device__ __forceinline__ void issue_tile_loads(uint8_t* smem, int a_bytes, int b_bytes, int wave,
-                                                 const uint8_t* const (&a_src)[A_LOADS],
-                                                 const uint8_t* const (&b_src)[B_LOADS], int ks, int64_t b_step,
-                                                 int buf) {
+// Retire this wave's VMEM loads older than the N most recent ones and all of
+// its LDS reads, then meet every other wave.  The wait is the compiler-visible
+// builtin (keeps the compiler's counter bookkeeping exact); the barrier is a
+// bare s_barrier with a memory clobber, since __syncthreads()'s release fence
+// would also drain every in-flight stage of LDS-bound loads.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
 #if defined(__HIP_DEVICE_COMPILE__)
-  uint8_t* a_dst = smem + buf * (a_bytes + b_bytes);
-  uint8_t* b_dst = a_dst + a_bytes;
-#pragma unroll
-  for (int j = 0; j < A_LOADS; ++j)
-    __builtin_amdgcn_global_load_lds(a_src[j] + (int64_t)ks * 128, a_dst + (j * 4 + wave) * 1024, 16, 0, 0);
-#pragma unroll
-  for (int j = 0; j < B_LOADS; ++j)
-    __builtin_amdgcn_global_load_lds(b_src[j] + (int64_t)ks * b_step, b_dst + (j * 4 + wave) * 1024, 16, 0, 0);
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  // gfx9 s_waitcnt: vmcnt[3:0] + vmcnt[5:4] at [15:14], expcnt[6:4] = 7 (none), lgkmcnt[11:8] = 0
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  asm volatile("s_barrier" ::: "memory");
 #endif
 }
 
-// Scale bytes of K block ks for this lane's rows (A) and columns (B).
-template <int MT, int NT>
-__device__ __forceinline__ void load_scales(const uint8_t* const (&sa_src)[MT], const uint8_t* const (&sb_src)[NT],
-                                            int64_t sb_step, int ks, int (&sa)[MT], int (&sb)[NT]) {
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) sa[mt] = sa_src[mt][ks];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) sb[nt] = sb_src[nt][(int64_t)ks * sb_step];
-}
-
-template <int BM, int BN, int AFMT, int BFMT, bool BKN, bool BROW>
-__global__ __launch_bounds__(kThreads) void gemm_bs_kernel(
+template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ SA,
     const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ SB, void* __restrict__ C,
     int64_t ldc, int out_bf16, int tiles_m, int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-  constexpr int WM = BM / 2, WN = BN / 2;       // per-wave tile
-  constexpr int MT = WM / 16, NT = WN / 16;     // 16x16 MFMA tiles per wave
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-  constexpr int A_LOADS = A_BYTES / (kThreads * 16);
-  constexpr int B_LOADS = B_BYTES / (kThreads * 16);
-  constexpr int CPR = BN / 16;                  // 16-byte chunks per KN tile row
-  static_assert(BM % 32 == 0 && BN % 32 == 0, "tile");
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int MT = WM / 32, NT = WN / 32;          // 32x32 MFMA tiles per wave
+  // Ring slot: A tile [BM][64 B], B tile, then (used by even stages) one
+  // dword per row of A and per column of B holding that K block's scale byte.
+  constexpr int A_ST = BM * BK, B_ST = BN * BK;
+  constexpr int SA_OFF = A_ST + B_ST, SB_OFF = SA_OFF + kThreads * 4, ST = SB_OFF + kThreads * 4;
+  constexpr int A_LOADS = A_ST / (kThreads * 16), B_LOADS = B_ST / (kThreads * 16);
+  constexpr int LOADS = A_LOADS + B_LOADS;           // tile VMEM instructions per stage per thread
+  constexpr int SLOADS = 2;                          // scale VMEM instructions per K block
+  constexpr int CPR = BN / 16;
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && A_LOADS >= 1 && B_LOADS >= 1, "tile");
+  static_assert(BM <= kThreads && BN <= kThreads, "one scale slot per thread");
+  static_assert(3 * LOADS + 2 * SLOADS <= 63, "vmcnt range");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (A_BYTES + B_BYTES)];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * ST];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- tile selection: XCD-contiguous bands, grouped rows within a band
+  // ---- tile of this workgroup
   int wg = blockIdx.x;
   const int nwg = tiles_m * tiles_n;
   if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
@@ -122,160 +120,257 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(
   const int first = group * GROUP;
   const int gsz = min(tiles_m - first, GROUP);
   const int within = wg - group * GROUP * tiles_n;
-  const int tm = first + within % gsz;
-  const int tn = within / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = (first + within % gsz) * BM;
+  const int n0 = (within / gsz) * BN;
 
-  const int nkb = K >> 7;
+  const int nst = K / BK;   // stages (even: K % 128 == 0)
+  const int nkb = K >> 7;   // 128-wide scale blocks
   const int nnb = (N + 127) >> 7;
 
-  // ---- per-lane global source addresses for the LDS loads (K block 0)
-  const uint8_t* a_src[A_LOADS];
+  // ---- HBM -> LDS sources: uniform tile bases + per-lane 32-bit offsets.
+  // Each wave-instruction fills 1 KB of LDS in lane order; the offsets encode
+  // the row swizzle.  Rows past M / N are clamped (their results are dropped).
+  const uint8_t* a_base = A + (int64_t)m0 * lda;
+  uint32_t a_off[A_LOADS];
 #pragma unroll
   for (int j = 0; j < A_LOADS; ++j) {
-    const int row = (j * 4 + wave) * 8 + (lane >> 3);
-    const int lc = (lane & 7) ^ swz_rows(row);
-    const int gm = min(m0 + row, M - 1);
-    a_src[j] = A + (int64_t)gm * lda + lc * 16;
+    const int row = (j * 4 + wave) * 16 + (lane >> 2);
+    const int lc = (lane & 3) ^ swz64(row);
+    a_off[j] = (uint32_t)((min(m0 + row, M - 1) - m0) * lda + lc * 16);
   }
-  const uint8_t* b_src[B_LOADS];
+  const uint8_t* b_base = BKN ? B : B + (int64_t)n0 * ldb;
+  uint32_t b_off[B_LOADS];
 #pragma unroll
   for (int j = 0; j < B_LOADS; ++j) {
     if (!BKN) {
-      const int row = (j * 4 + wave) * 8 + (lane >> 3);
-      const int lc = (lane & 7) ^ swz_rows(row);
-      const int gn = min(n0 + row, N - 1);
-      b_src[j] = B + (int64_t)gn * ldb + lc * 16;
+      const int row = (j * 4 + wave) * 16 + (lane >> 2);
+      const int lc = (lane & 3) ^ swz64(row);
+      b_off[j] = (uint32_t)((min(n0 + row, N - 1) - n0) * ldb + lc * 16);
     } else {
       constexpr int RPI = 64 / CPR;  // k rows per wave-instruction
       const int krow = (j * 4 + wave) * RPI + lane / CPR;
       const int lc = (lane % CPR) ^ swz_kn<CPR>(krow);
       int col = n0 + lc * 16;
       if (col >= N) col = 0;
-      b_src[j] = B + (int64_t)krow * ldb + col;
+      b_off[j] = (uint32_t)(krow * ldb + col);
     }
   }
-  const int64_t b_step = BKN ? (int64_t)128 * ldb : 128;
+  const int64_t b_step = BKN ? (int64_t)BK * ldb : BK;
 
-  // ---- scale sources
-  const uint8_t* sa_src[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int gm = min(m0 + wm * WM + mt * 16 + (lane & 15), M - 1);
-    sa_src[mt] = SA + (int64_t)gm * nkb;
+  // Scale sources: thread t fetches the scale byte of tile row t (A) and of
+  // tile column t (B) for a K block; the byte lands zero-extended in dword t
+  // of the slot's scale area (the LDS layout of 1-byte LDS-bound loads).
+  const uint8_t* sa_base = SA + (int64_t)m0 * nkb;
+  const uint32_t sa_off = (uint32_t)((min(m0 + tid, M - 1) - m0) * nkb);
+  const uint8_t* sb_base;
+  uint32_t sb_off;
+  int sb_step;
+  if (BROW) {
+    sb_base = SB + (int64_t)n0 * nkb;
+    sb_off = (uint32_t)((min(n0 + tid, N - 1) - n0) * nkb);
+    sb_step = 1;
+  } else {
+    const int nb = min((n0 + tid) >> 7, nnb - 1);
+    sb_base = SB;
+    sb_off = (uint32_t)(BKN ? nb : nb * nkb);
+    sb_step = BKN ? nnb : 1;
   }
-  const uint8_t* sb_src[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    if (BROW) {
-      const int gn = min(n0 + wn * WN + nt * 16 + (lane & 15), N - 1);
-      sb_src[nt] = SB + (int64_t)gn * nkb;
-    } else {
-      const int nb = min((n0 + wn * WN + nt * 16) >> 7, nnb - 1);
-      sb_src[nt] = BKN ? SB + nb : SB + (int64_t)nb * nkb;
+
+  // All LDS-bound loads of stage st into ring slot st % STAGES; an even stage
+  // also carries the scale bytes of its K block.
+  auto dma = [&](int st) {
+    uint8_t* slot = smem + (st % STAGES) * ST;
+    if ((st & 1) == 0) {
+      const int kb = st >> 1;
+      __builtin_amdgcn_global_load_lds(sa_base + kb + sa_off, slot + SA_OFF + wave * 256, 1, 0, 0);
+      __builtin_amdgcn_global_load_lds(sb_base + (int64_t)kb * sb_step + sb_off, slot + SB_OFF + wave * 256, 1,
+                                       0, 0);
     }
-  }
-  const int64_t sb_step = (!BROW && BKN) ? nnb : 1;
+    const uint8_t* ab = a_base + (int64_t)st * BK;
+    const uint8_t* bb = b_base + (int64_t)st * b_step;
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j)
+      __builtin_amdgcn_global_load_lds(ab + a_off[j], slot + (j * 4 + wave) * 1024, 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j)
+      __builtin_amdgcn_global_load_lds(bb + b_off[j], slot + A_ST + (j * 4 + wave) * 1024, 16, 0, 0);
+  };
 
-  int sa_nxt[MT], sb_nxt[NT];
+  int sa_cur[MT], sb_cur[NT], sa_nxt[MT], sb_nxt[NT];
+  // Scale operands of the K block whose even stage sits in slot st % STAGES.
+  auto read_scales = [&](int st, int (&sa)[MT], int (&sb)[NT]) {
+    const uint8_t* slot = smem + (st % STAGES) * ST;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      sa[mt] = *reinterpret_cast<const int*>(slot + SA_OFF + (wm * WM + mt * 32 + (lane & 31)) * 4);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      sb[nt] = *reinterpret_cast<const int*>(slot + SB_OFF + (wn * WN + nt * 32 + (lane & 31)) * 4);
+  };
 
-  v4f acc[MT][NT];
+  v16f acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  if (nkb > 0) {
-    issue_tile_loads<A_LOADS, B_LOADS>(smem, A_BYTES, B_BYTES, wave, a_src, b_src, 0, b_step, 0);
-    load_scales<MT, NT>(sa_src, sb_src, sb_step, 0, sa_nxt, sb_nxt);
-  }
-
-  const int g = lane >> 4;
-  for (int ks = 0; ks < nkb; ++ks) {
-    const int buf = ks & 1;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS loads for block ks have landed
-    __syncthreads();                // ... and every other wave's; buffer buf^1 is free
-    int sa_cur[MT], sb_cur[NT];
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) sa_cur[mt] = sa_nxt[mt];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sb_cur[nt] = sb_nxt[nt];
+      for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.0f;
 
-    const uint8_t* a_lds = smem + buf * (A_BYTES + B_BYTES);
-    const uint8_t* b_lds = a_lds + A_BYTES;
-    v8i af[MT], bfr[NT];
+  const int g = lane >> 5;
+  // Fragments of one stage from its LDS buffer.  Lane l holds, for its row
+  // (A) / column (B) l & 31, bytes k = 32*(l>>5) .. +31 of the 64-wide stage,
+  // in k order, for both operands (the pairing the MFMA needs).
+  auto read_frags = [&](int st, v8i (&af)[MT], v8i (&bfr)[NT]) {
+    const uint8_t* a_lds = smem + (st % STAGES) * ST;
+    const uint8_t* b_lds = a_lds + A_ST;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int r = wm * WM + mt * 16 + (lane & 15);
-      const int sw = swz_rows(r);
-      const v4i lo = *reinterpret_cast<const v4i*>(a_lds + r * 128 + (((2 * g) ^ sw) << 4));
-      const v4i hi = *reinterpret_cast<const v4i*>(a_lds + r * 128 + (((2 * g + 1) ^ sw) << 4));
+      const int r = wm * WM + mt * 32 + (lane & 31);
+      const int sw = swz64(r);
+      const v4i lo = *reinterpret_cast<const v4i*>(a_lds + r * 64 + (((2 * g) ^ sw) << 4));
+      const v4i hi = *reinterpret_cast<const v4i*>(a_lds + r * 64 + (((2 * g + 1) ^ sw) << 4));
       af[mt] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       if (!BKN) {
-        const int r = wn * WN + nt * 16 + (lane & 15);
-        const int sw = swz_rows(r);
-        const v4i lo = *reinterpret_cast<const v4i*>(b_lds + r * 128 + (((2 * g) ^ sw) << 4));
-        const v4i hi = *reinterpret_cast<const v4i*>(b_lds + r * 128 + (((2 * g + 1) ^ sw) << 4));
+        const int r = wn * WN + nt * 32 + (lane & 31);
+        const int sw = swz64(r);
+        const v4i lo = *reinterpret_cast<const v4i*>(b_lds + r * 64 + (((2 * g) ^ sw) << 4));
+        const v4i hi = *reinterpret_cast<const v4i*>(b_lds + r * 64 + (((2 * g + 1) ^ sw) << 4));
         bfr[nt] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       } else {
-        const int nsub = (wn * WN + nt * 16) >> 4;
+        // 16-lane group grp covers columns 16*(grp&1) .. +15 and k half grp>>1;
+        // lane pair (2j, 2j+1) points at row k of that block, bytes 0-7 / 8-15.
+        const int grp = lane >> 4;
+        const int nsub = ((wn * WN + nt * 32) >> 4) + (grp & 1);
+        const int kg = grp >> 1;
         const int j = (lane & 15) >> 1, half = lane & 1;
         v2i part[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int k = 32 * g + 8 * t + j;
-          const int off = k * BN + ((nsub ^ (int)swz_kn<CPR>(k)) << 4) + half * 8;
+          const int k = 32 * kg + 8 * t + j;
+          const int off = k * BN + ((nsub ^ swz_kn<CPR>(k)) << 4) + half * 8;
           part[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(b_lds + off));
         }
         bfr[nt] = v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
       }
     }
-
-    if (ks + 1 < nkb) {
-      issue_tile_loads<A_LOADS, B_LOADS>(smem, A_BYTES, B_BYTES, wave, a_src, b_src, ks + 1, b_step, buf ^ 1);
-      load_scales<MT, NT>(sa_src, sb_src, sb_step, ks + 1, sa_nxt, sb_nxt);
-    }
-
+  };
+  constexpr int DS_PER_STAGE = 2 * MT + (BKN ? 4 : 2) * NT;
+  constexpr int DS_PER_MFMA = (DS_PER_STAGE + MT * NT - 1) / (MT * NT);
+  // MFMAs of one stage from fragment registers; the next stage's LDS reads
+  // (issued just before) are interleaved into the MFMA stream.
+  auto mfmas = [&](const v8i (&af)[MT], const v8i (&bfr)[NT]) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             bfr[nt], af[mt], acc[mt][nt], BFMT, AFMT, 0, sb_cur[nt], 0, sa_cur[mt]);
+#pragma unroll
+    for (int i = 0; i < MT * NT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, DS_PER_MFMA, 0);  // then LDS reads
+    }
+  };
+
+  // ---- prologue: STAGES stages of loads in flight (scale bytes ride with
+  // the even stages), then stage 0's fragments and K block 0's scales.
+  static_assert(STAGES == 4, "the waits below assume a ring of four stages");
+#pragma unroll
+  for (int st = 0; st < STAGES; ++st)
+    if (st < nst) dma(st);
+  v8i fa0[MT], fb0[NT], fa1[MT], fb1[NT];
+  if (nst > 0) {
+    // younger than stage 0: stages 1..3 = 3 tile batches + one scale batch (stage 2)
+    if (nst >= 4) wait_vm_barrier<LOADS * 3 + SLOADS>();
+    else wait_vm_barrier<LOADS>();  // nst == 2: only stage 1 is younger
+    read_frags(0, fa0, fb0);
+    read_scales(0, sa_cur, sb_cur);
   }
 
-  // ---- epilogue: lane holds C[m][nb .. nb+3]
+  // ---- steady state, one 128-wide K block (two stages) per iteration.  At
+  // the top of stage st: (1) stage st+1 has landed for every wave and every
+  // wave holds stage st's fragments, so (2) slot st % STAGES is refilled with
+  // stage st + STAGES; (3) stage st's MFMAs run while stage st+1's fragments
+  // (and, for an even st+1, its K block's scales) are read.  Two younger
+  // stages, one of them even, are in flight at each wait.
+  constexpr int W2 = LOADS * 2 + SLOADS;
+  const int main_kb = nkb - 2;
+#pragma nounroll
+  for (int kb = 0; kb < main_kb; ++kb) {
+    const int st = 2 * kb;
+    wait_vm_barrier<W2>();
+    dma(st + STAGES);
+    read_frags(st + 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    wait_vm_barrier<W2>();
+    dma(st + 1 + STAGES);
+    read_frags(st + 2, fa0, fb0);
+    read_scales(st + 2, sa_nxt, sb_nxt);
+    mfmas(fa1, fb1);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) sa_cur[mt] = sa_nxt[mt];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) sb_cur[nt] = sb_nxt[nt];
+  }
+  // ---- drain: the last (up to) two K blocks, no further loads
+  if (nkb >= 2) {
+    const int st = nst - 4;
+    wait_vm_barrier<W2>();  // younger than st+1: stages st+2 (even), st+3
+    read_frags(st + 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    wait_vm_barrier<LOADS>();  // younger than st+2: stage st+3
+    read_frags(st + 2, fa0, fb0);
+    read_scales(st + 2, sa_nxt, sb_nxt);
+    mfmas(fa1, fb1);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) sa_cur[mt] = sa_nxt[mt];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) sb_cur[nt] = sb_nxt[nt];
+  }
+  if (nkb >= 1) {
+    const int st = nst - 2;
+    wait_vm_barrier<0>();
+    read_frags(st + 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    mfmas(fa1, fb1);
+  }
+
+  // ---- epilogue: lane holds C[m][nb .. nb+3] for nb = tile col + 8q + 4*(lane>>5)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int m = m0 + wm * WM + mt * 16 + (lane & 15);
+    const int m = m0 + wm * WM + mt * 32 + (lane & 31);
     if (m >= M) continue;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int nb = n0 + wn * WN + nt * 16 + g * 4;
-      const v4f v = acc[mt][nt];
-      if (!out_bf16) {
-        float* crow = reinterpret_cast<float*>(C) + (int64_t)m * ldc;
-        if (nb + 3 < N) {
-          *reinterpret_cast<v4f*>(crow + nb) = v;
-        } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (nb + i < N) crow[nb + i] = v[i];
-        }
-      } else {
-        uint16_t* crow = reinterpret_cast<uint16_t*>(C) + (int64_t)m * ldc;
-        if (nb + 3 < N) {
-          uint2 o;
-          o.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-          o.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-          *reinterpret_cast<uint2*>(crow + nb) = o;
-        } else {
+      for (int q = 0; q < 4; ++q) {
+        const int nb = n0 + wn * WN + nt * 32 + 8 * q + 4 * g;
+        const v4f v = v4f{acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2],
+                          acc[mt][nt][4 * q + 3]};
+        if (!out_bf16) {
+          float* crow = reinterpret_cast<float*>(C) + (int64_t)m * ldc;
+          if (nb + 3 < N) {
+            *reinterpret_cast<v4f*>(crow + nb) = v;
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (nb + i < N) crow[nb + i] = (uint16_t)bf16_rne(v[i]);
+            for (int i = 0; i < 4; ++i)
+              if (nb + i < N) crow[nb + i] = v[i];
+          }
+        } else {
+          uint16_t* crow = reinterpret_cast<uint16_t*>(C) + (int64_t)m * ldc;
+          if (nb + 3 < N) {
+            uint2 o;
+            o.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+            o.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+            *reinterpret_cast<uint2*>(crow + nb) = o;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (nb + i < N) crow[nb + i] = (uint16_t)bf16_rne(v[i]);
+          }
         }
       }
     }
@@ -283,27 +378,44 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(
 #endif
 }
 
-template <int BM, int BN, int AFMT, int BFMT, bool BKN, bool BROW>
+template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW>
 void launch_tile(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
                  const uint8_t* b, int64_t ldb, const uint8_t* sb, void* c, int64_t ldc, int c_dtype,
                  hipStream_t stream) {
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bs_kernel<BM, BN, AFMT, BFMT, BKN, BROW>), dim3(tiles_m * tiles_n), dim3(kThreads),
-                     0, stream, (int)M, (int)N, (int)K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype == 1 ? 1 : 0,
-                     tiles_m, tiles_n);
+  hipLaunchKernelGGL((gemm_bs_kernel<BM, BN, STAGES, AFMT, BFMT, BKN, BROW>), dim3(tiles_m * tiles_n),
+                     dim3(kThreads), 0, stream, (int)M, (int)N, (int)K, a, lda, sa, b, ldb, sb, c, ldc,
+                     c_dtype == 1 ? 1 : 0, tiles_m, tiles_n);
+}
+
+// Tile choice: 256x256 (128x128 per wave, the lowest LDS traffic per MFMA) when
+// there are enough tiles to cover the 256 CUs, else 128x128.  Building with
+// -DMXFP8_GEMM_TILE=128 or 256 pins one of them (for tuning).
+#ifndef MXFP8_GEMM_TILE
+#define MXFP8_GEMM_TILE 0
+#endif
+template <int AFMT, int BFMT, bool BKN, bool BROW>
+void launch_shape(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
+                  const uint8_t* b, int64_t ldb, const uint8_t* sb, void* c, int64_t ldc, int c_dtype,
+                  hipStream_t stream) {
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const bool big = MXFP8_GEMM_TILE == 256 || (MXFP8_GEMM_TILE == 0 && big_tiles >= 256);
+  if (big)
+    launch_tile<256, 256, 4, AFMT, BFMT, BKN, BROW>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+  else
+    launch_tile<128, 128, 4, AFMT, BFMT, BKN, BROW>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
 }
 
 template <int AFMT, int BFMT>
 void launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
                 const uint8_t* b, int64_t ldb, int b_layout, const uint8_t* sb, int b_scale_mode, void* c,
                 int64_t ldc, int c_dtype, hipStream_t stream) {
-  constexpr int BM = 128, BN = 128;
   if (b_layout == 1)
-    launch_tile<BM, BN, AFMT, BFMT, true, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+    launch_shape<AFMT, BFMT, true, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
   else if (b_scale_mode == 1)
-    launch_tile<BM, BN, AFMT, BFMT, false, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+    launch_shape<AFMT, BFMT, false, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
   else
-    launch_tile<BM, BN, AFMT, BFMT, false, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+    launch_shape<AFMT, BFMT, false, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
 }
 
 }  // namespace gemm_detail
