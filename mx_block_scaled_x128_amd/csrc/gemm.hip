@@ -80,11 +80,59 @@ template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert(N >= 0 && N <= 63, "vmcnt");
+  __builtin_amdgcn_sched_barrier(0);  // nothing (MFMAs included) crosses the stage boundary
   // gfx9 s_waitcnt: vmcnt[3:0] + vmcnt[5:4] at [15:14], expcnt[6:4] = 7 (none), lgkmcnt[11:8] = 0
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
   asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 #endif
 }
+
+// Hides a value from the optimiser.  LDS read addresses are written as
+// ring_slot + opaque lane offset + constant, so every read stays a short
+// address expression on one named ring array: the backend then knows which
+// slot each read touches and waits only for the loads into that slot.  (A
+// long chain of partial sums shared between slots loses that knowledge and
+// each read would drain every LDS-bound load in flight.)
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(x));
+#endif
+  return x;
+}
+
+// Same for a wave-uniform pointer, kept in scalar registers.  HBM sources
+// are written as (this per-stage uniform base) + 32-bit lane offset, which
+// selects the scalar-base + vector-offset load form; otherwise loop-invariant
+// code motion re-associates them into one 64-bit vector address per load,
+// which costs two VGPRs each for the life of the loop.
+__device__ __forceinline__ const uint8_t* uniform_opaque(const uint8_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+s"(p));
+#endif
+  return p;
+}
+
+// Lets the last MFMA retire before anything reads its accumulators.  The
+// compiler's wait between a 32x32x64 scaled MFMA and a read of its result is
+// too short for the last result registers: without this pad the epilogue
+// stored acc[..][15] of the final MFMA without the last stage's contribution
+// (two output columns per tile, reproducibly).  64 wait states cover the
+// whole 16-pass operation.  Called at the end of every path out of the K
+// loop, so that the accumulator copies the compiler places where the paths
+// merge come after it.
+__device__ __forceinline__ void mfma_retire_pad() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
+// MFMAs a stage issues before its first LDS read or HBM->LDS load.
+#ifndef MXFP8_GEMM_LEAD
+#define MXFP8_GEMM_LEAD 0
+#endif
 
 template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
@@ -106,9 +154,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   static_assert(BM <= kThreads && BN <= kThreads, "one scale slot per thread");
   static_assert(3 * LOADS + 2 * SLOADS <= 63, "vmcnt range");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * ST];
+  // The LDS ring: one array per slot.  Every access names its slot with a
+  // compile-time constant (the loops below are unrolled so that it does), so
+  // the compiler can tell slots apart: it then does not drain in-flight
+  // LDS-bound loads before reading a different slot (it must assume that a
+  // read may alias an in-flight load into the same array).
+  static_assert(STAGES == 4, "four ring slots");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[ST];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[ST];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[ST];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[ST];
+  auto slot_ptr = [&](int sl) __attribute__((always_inline)) -> uint8_t* { return sl == 0 ? ring0 : sl == 1 ? ring1 : sl == 2 ? ring2 : ring3; };
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // known uniform: LDS destinations stay scalar
   const int wm = wave >> 1, wn = wave & 1;
 
   // ---- tile of this workgroup
@@ -176,36 +235,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
     sb_step = BKN ? nnb : 1;
   }
 
-  // All LDS-bound loads of stage st into ring slot st % STAGES; an even stage
-  // also carries the scale bytes of its K block.
-  auto dma = [&](int st) {
-    uint8_t* slot = smem + (st % STAGES) * ST;
-    if ((st & 1) == 0) {
-      const int kb = st >> 1;
-      __builtin_amdgcn_global_load_lds(sa_base + kb + sa_off, slot + SA_OFF + wave * 256, 1, 0, 0);
-      __builtin_amdgcn_global_load_lds(sb_base + (int64_t)kb * sb_step + sb_off, slot + SB_OFF + wave * 256, 1,
-                                       0, 0);
+  // LDS-bound loads of stage st into ring slot sl (= st % STAGES), one
+  // instruction per item: items 0..SLOADS-1 are the scale bytes (even stages
+  // only), then A_LOADS tile loads of A and B_LOADS of B.
+  constexpr int DMA_ITEMS = SLOADS + A_LOADS + B_LOADS;
+  struct Src {
+    const uint8_t *a, *b, *sa, *sb;
+  };
+  auto dma_src = [&](int st) __attribute__((always_inline)) {
+    const int kb = st >> 1;
+    Src src;
+    src.a = uniform_opaque(a_base + (int64_t)st * BK);
+    src.b = uniform_opaque(b_base + (int64_t)st * b_step);
+    src.sa = uniform_opaque(sa_base + kb);
+    src.sb = uniform_opaque(sb_base + (int64_t)kb * sb_step);
+    return src;
+  };
+  auto dma_item = [&](int sl, const Src& src, int item) __attribute__((always_inline)) {
+    uint8_t* slot = slot_ptr(sl);
+    if (item == 0) {
+      __builtin_amdgcn_global_load_lds(src.sa + sa_off, slot + SA_OFF + wave * 256, 1, 0, 0);
+    } else if (item == 1) {
+      __builtin_amdgcn_global_load_lds(src.sb + sb_off, slot + SB_OFF + wave * 256, 1, 0, 0);
+    } else if (item < SLOADS + A_LOADS) {
+      const int j = item - SLOADS;
+      __builtin_amdgcn_global_load_lds(src.a + a_off[j], slot + (j * 4 + wave) * 1024, 16, 0, 0);
+    } else {
+      const int j = item - SLOADS - A_LOADS;
+      __builtin_amdgcn_global_load_lds(src.b + b_off[j], slot + A_ST + (j * 4 + wave) * 1024, 16, 0, 0);
     }
-    const uint8_t* ab = a_base + (int64_t)st * BK;
-    const uint8_t* bb = b_base + (int64_t)st * b_step;
+  };
+  auto dma = [&](int sl, int st) __attribute__((always_inline)) {
+    const Src src = dma_src(st);
 #pragma unroll
-    for (int j = 0; j < A_LOADS; ++j)
-      __builtin_amdgcn_global_load_lds(ab + a_off[j], slot + (j * 4 + wave) * 1024, 16, 0, 0);
-#pragma unroll
-    for (int j = 0; j < B_LOADS; ++j)
-      __builtin_amdgcn_global_load_lds(bb + b_off[j], slot + A_ST + (j * 4 + wave) * 1024, 16, 0, 0);
+    for (int item = 0; item < DMA_ITEMS; ++item)
+      if (item >= SLOADS || (st & 1) == 0) dma_item(sl, src, item);
   };
 
-  int sa_cur[MT], sb_cur[NT], sa_nxt[MT], sb_nxt[NT];
-  // Scale operands of the K block whose even stage sits in slot st % STAGES.
-  auto read_scales = [&](int st, int (&sa)[MT], int (&sb)[NT]) {
-    const uint8_t* slot = smem + (st % STAGES) * ST;
+  // Scale operands of the K block whose even stage sits in slot sl.
+  const uint32_t sa_rd = opaque(SA_OFF + (wm * WM + (lane & 31)) * 4);
+  const uint32_t sb_rd = opaque(SB_OFF + (wn * WN + (lane & 31)) * 4);
+  auto read_scales = [&](int sl, int (&sa)[MT], int (&sb)[NT]) __attribute__((always_inline)) {
+    const uint8_t* slot = slot_ptr(sl);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      sa[mt] = *reinterpret_cast<const int*>(slot + SA_OFF + (wm * WM + mt * 32 + (lane & 31)) * 4);
+    for (int mt = 0; mt < MT; ++mt) sa[mt] = *reinterpret_cast<const int*>(slot + sa_rd + mt * 128);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      sb[nt] = *reinterpret_cast<const int*>(slot + SB_OFF + (wn * WN + nt * 32 + (lane & 31)) * 4);
+    for (int nt = 0; nt < NT; ++nt) sb[nt] = *reinterpret_cast<const int*>(slot + sb_rd + nt * 128);
   };
 
   v16f acc[MT][NT];
@@ -219,123 +294,182 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   const int g = lane >> 5;
   // Fragments of one stage from its LDS buffer.  Lane l holds, for its row
   // (A) / column (B) l & 31, bytes k = 32*(l>>5) .. +31 of the 64-wide stage,
-  // in k order, for both operands (the pairing the MFMA needs).
-  auto read_frags = [&](int st, v8i (&af)[MT], v8i (&bfr)[NT]) {
-    const uint8_t* a_lds = smem + (st % STAGES) * ST;
-    const uint8_t* b_lds = a_lds + A_ST;
+  // in k order, for both operands (the pairing the MFMA needs).  One LDS read
+  // per item: A items 2*mt + half (16 bytes each), then B items (two 16-byte
+  // halves per fragment, or four 8-byte transposed parts when B is [K][N]).
+  constexpr int B_PARTS = BKN ? 4 : 2;
+  constexpr int DS_ITEMS = 2 * MT + B_PARTS * NT;
+  // Per-lane read offsets within a slot (the 32-row / 32-column step of a
+  // fragment and the 8-row step of a transposed part are added as constants:
+  // neither changes the swizzle, which depends only on low row bits).
+  uint32_t a_rd[2], b_rd[BKN ? NT : 2];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int r = wm * WM + mt * 32 + (lane & 31);
-      const int sw = swz64(r);
-      const v4i lo = *reinterpret_cast<const v4i*>(a_lds + r * 64 + (((2 * g) ^ sw) << 4));
-      const v4i hi = *reinterpret_cast<const v4i*>(a_lds + r * 64 + (((2 * g + 1) ^ sw) << 4));
-      af[mt] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  for (int half = 0; half < 2; ++half) {
+    const int r = wm * WM + (lane & 31);
+    a_rd[half] = opaque(r * 64 + (((2 * g + half) ^ swz64(r)) << 4));
+  }
+  if (!BKN) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int r = wn * WN + (lane & 31);
+      b_rd[half] = opaque(A_ST + r * 64 + (((2 * g + half) ^ swz64(r)) << 4));
     }
+  } else {
+    // 16-lane group grp covers columns 16*(grp&1) .. +15 and k half grp>>1;
+    // lane pair (2j, 2j+1) points at row k of that block, bytes 0-7 / 8-15.
+    const int grp = lane >> 4, j = (lane & 15) >> 1, half = lane & 1;
+    const int k = 32 * (grp >> 1) + j;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      if (!BKN) {
-        const int r = wn * WN + nt * 32 + (lane & 31);
-        const int sw = swz64(r);
-        const v4i lo = *reinterpret_cast<const v4i*>(b_lds + r * 64 + (((2 * g) ^ sw) << 4));
-        const v4i hi = *reinterpret_cast<const v4i*>(b_lds + r * 64 + (((2 * g + 1) ^ sw) << 4));
-        bfr[nt] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      } else {
-        // 16-lane group grp covers columns 16*(grp&1) .. +15 and k half grp>>1;
-        // lane pair (2j, 2j+1) points at row k of that block, bytes 0-7 / 8-15.
-        const int grp = lane >> 4;
-        const int nsub = ((wn * WN + nt * 32) >> 4) + (grp & 1);
-        const int kg = grp >> 1;
-        const int j = (lane & 15) >> 1, half = lane & 1;
-        v2i part[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int k = 32 * kg + 8 * t + j;
-          const int off = k * BN + ((nsub ^ swz_kn<CPR>(k)) << 4) + half * 8;
-          part[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(b_lds + off));
-        }
-        bfr[nt] = v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
-      }
+    for (int nt = 0; nt < (BKN ? NT : 0); ++nt) {
+      const int nsub = ((wn * WN + nt * 32) >> 4) + (grp & 1);
+      b_rd[nt] = opaque(A_ST + k * BN + ((nsub ^ swz_kn<CPR>(k)) << 4) + half * 8);
+    }
+  }
+  auto ds_item = [&](int sl, int item, v8i (&af)[MT], v8i (&bfr)[NT]) __attribute__((always_inline)) {
+    const uint8_t* lds = slot_ptr(sl);
+    if (item < 2 * MT) {
+      const int mt = item >> 1, half = item & 1;
+      const v4i v = *reinterpret_cast<const v4i*>(lds + a_rd[half] + mt * 2048);
+      if (half == 0) af[mt].s0123 = v;
+      else af[mt].s4567 = v;
+    } else if (!BKN) {
+      const int nt = (item - 2 * MT) >> 1, half = item & 1;
+      const v4i v = *reinterpret_cast<const v4i*>(lds + b_rd[half] + nt * 2048);
+      if (half == 0) bfr[nt].s0123 = v;
+      else bfr[nt].s4567 = v;
+    } else {
+      // part t: k rows 8t .. 8t+7 of the lane's k half
+      const int nt = (item - 2 * MT) >> 2, t = (item - 2 * MT) & 3;
+      const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(lds + b_rd[nt] + 8 * t * BN));
+      if (t == 0) bfr[nt].s01 = v;
+      else if (t == 1) bfr[nt].s23 = v;
+      else if (t == 2) bfr[nt].s45 = v;
+      else bfr[nt].s67 = v;
     }
   };
-  constexpr int DS_PER_STAGE = 2 * MT + (BKN ? 4 : 2) * NT;
-  constexpr int DS_PER_MFMA = (DS_PER_STAGE + MT * NT - 1) / (MT * NT);
-  // MFMAs of one stage from fragment registers; the next stage's LDS reads
-  // (issued just before) are interleaved into the MFMA stream.
-  auto mfmas = [&](const v8i (&af)[MT], const v8i (&bfr)[NT]) {
+  auto read_frags = [&](int sl, v8i (&af)[MT], v8i (&bfr)[NT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int item = 0; item < DS_ITEMS; ++item) ds_item(sl, item, af, bfr);
+  };
+
+  // One stage as an explicit instruction stream.  The first LEAD MFMAs go
+  // out alone; after that each MFMA is followed by its share of the next
+  // stage's LDS reads (all within the first half of the remaining steps, so
+  // they land well before the next barrier) and of the HBM->LDS loads, spread
+  // evenly (one per MFMA on the 256-wide tile: a burst would stall this
+  // wave's in-order issue and starve its MFMA pipe).  sched_barrier(0) keeps
+  // the order.
+  constexpr int MFMAS = MT * NT;
+  constexpr int LEAD = MXFP8_GEMM_LEAD;
+  constexpr int STEPS = MFMAS - LEAD;
+  static_assert(STEPS >= 2, "tile");
+  constexpr int DS_PER_STEP = (DS_ITEMS + STEPS / 2 - 1) / (STEPS / 2);
+  constexpr int DMA_PER_STEP = (DMA_ITEMS + STEPS - 1) / STEPS;
+  // Stage st lives in slot sl and multiplies with the scales (csa, csb).
+  // do_dma: refill slot sl with stage st + STAGES (same parity as st).
+  // do_ds: read stage st+1's fragments from the next slot into (na, nb).
+  // do_sc: also read the scales stored with stage st+1 (an even stage: a new
+  // K block) into (nsa, nsb).
+  auto stage = [&](int sl, int st, bool do_dma, bool do_ds, bool do_sc, const v8i (&ca)[MT],
+                   const v8i (&cb)[NT], v8i (&na)[MT], v8i (&nb)[NT], const int (&csa)[MT],
+                   const int (&csb)[NT], int (&nsa)[MT], int (&nsb)[NT]) __attribute__((always_inline)) {
+    const bool even_dma = (st & 1) == 0;
+    const Src src = dma_src(st + STAGES);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            bfr[nt], af[mt], acc[mt][nt], BFMT, AFMT, 0, sb_cur[nt], 0, sa_cur[mt]);
+    for (int i = 0; i < MFMAS; ++i) {
+      const int mt = i / NT, nt = i % NT;
+      acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[nt], ca[mt], acc[mt][nt], BFMT, AFMT, 0,
+                                                                   csb[nt], 0, csa[mt]);
+      if (i >= LEAD) {
+        const int j = i - LEAD;
+        if (do_sc && j == 0) read_scales((sl + 1) & 3, nsa, nsb);
 #pragma unroll
-    for (int i = 0; i < MT * NT; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, DS_PER_MFMA, 0);  // then LDS reads
+        for (int d = 0; d < DS_PER_STEP; ++d) {
+          const int item = j * DS_PER_STEP + d;
+          if (do_ds && item < DS_ITEMS) ds_item((sl + 1) & 3, item, na, nb);
+        }
+#pragma unroll
+        for (int d = 0; d < DMA_PER_STEP; ++d) {
+          const int item = j * DMA_PER_STEP + d;
+          if (do_dma && item < DMA_ITEMS && (item >= SLOADS || even_dma)) dma_item(sl, src, item);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // ---- prologue: STAGES stages of loads in flight (scale bytes ride with
-  // the even stages), then stage 0's fragments and K block 0's scales.
-  static_assert(STAGES == 4, "the waits below assume a ring of four stages");
-#pragma unroll
-  for (int st = 0; st < STAGES; ++st)
-    if (st < nst) dma(st);
+  // Two register sets each for fragments (stage parity) and scales (K block
+  // parity); the code below alternates them, so nothing is copied.
   v8i fa0[MT], fb0[NT], fa1[MT], fb1[NT];
-  if (nst > 0) {
+  int sa0[MT], sb0[NT], sa1[MT], sb1[NT];
+
+  // Slots: stage st sits in slot (st + s0) % 4.  s0 is chosen so that the
+  // drain (the last two K blocks) always starts in slot 0; every loop body
+  // below then names its slots as constants.
+  constexpr int W2 = LOADS * 2 + SLOADS;
+  const int main_kb = nkb - 2;  // K blocks whose stages all refill the ring
+  const bool odd_main = main_kb > 0 && (main_kb & 1);
+
+  // ---- prologue: STAGES stages of loads in flight (scale bytes ride with
+  // the even stages), then stage 0's fragments and K block 0's scales (into
+  // the set the first block uses: set 1 when a lone main block precedes the
+  // paired loop, else set 0).
+  auto prologue = [&](int s0, int (&psa)[MT], int (&psb)[NT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < STAGES; ++i)
+      if (i < nst) dma((s0 + i) & 3, i);
     // younger than stage 0: stages 1..3 = 3 tile batches + one scale batch (stage 2)
     if (nst >= 4) wait_vm_barrier<LOADS * 3 + SLOADS>();
     else wait_vm_barrier<LOADS>();  // nst == 2: only stage 1 is younger
-    read_frags(0, fa0, fb0);
-    read_scales(0, sa_cur, sb_cur);
+    read_frags(s0, fa0, fb0);
+    read_scales(s0, psa, psb);
+  };
+  if (nst > 0) {
+    if (odd_main) prologue(2, sa1, sb1);
+    else prologue(0, sa0, sb0);
   }
 
-  // ---- steady state, one 128-wide K block (two stages) per iteration.  At
-  // the top of stage st: (1) stage st+1 has landed for every wave and every
-  // wave holds stage st's fragments, so (2) slot st % STAGES is refilled with
-  // stage st + STAGES; (3) stage st's MFMAs run while stage st+1's fragments
-  // (and, for an even st+1, its K block's scales) are read.  Two younger
-  // stages, one of them even, are in flight at each wait.
-  constexpr int W2 = LOADS * 2 + SLOADS;
-  const int main_kb = nkb - 2;
+  // ---- steady state.  At the top of stage st: (1) stage st+1 has landed for
+  // every wave and every wave holds stage st's fragments, so (2) stage st's
+  // slot is refilled with stage st + STAGES; (3) stage st's MFMAs run while
+  // stage st+1's fragments (and, for an even st+1, its K block's scales) are
+  // read.  Two younger stages, one of them even, are in flight at each wait.
+  // One K block = two stages starting at an even stage in slot sl (0 or 2),
+  // using scale set (csa, csb) and loading the next block's into (nsa, nsb).
+  auto main_block = [&](int sl, int st, const int (&csa)[MT], const int (&csb)[NT], int (&nsa)[MT],
+                        int (&nsb)[NT]) __attribute__((always_inline)) {
+    wait_vm_barrier<W2>();
+    stage(sl, st, true, true, false, fa0, fb0, fa1, fb1, csa, csb, nsa, nsb);
+    wait_vm_barrier<W2>();
+    stage(sl + 1, st + 1, true, true, true, fa1, fb1, fa0, fb0, csa, csb, nsa, nsb);
+  };
+  int kb = 0;
+  if (odd_main) {
+    main_block(2, 0, sa1, sb1, sa0, sb0);
+    kb = 1;
+  }
 #pragma nounroll
-  for (int kb = 0; kb < main_kb; ++kb) {
-    const int st = 2 * kb;
-    wait_vm_barrier<W2>();
-    dma(st + STAGES);
-    read_frags(st + 1, fa1, fb1);
-    mfmas(fa0, fb0);
-    wait_vm_barrier<W2>();
-    dma(st + 1 + STAGES);
-    read_frags(st + 2, fa0, fb0);
-    read_scales(st + 2, sa_nxt, sb_nxt);
-    mfmas(fa1, fb1);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) sa_cur[mt] = sa_nxt[mt];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sb_cur[nt] = sb_nxt[nt];
+  for (; kb < main_kb; kb += 2) {  // two K blocks: slots 0..3, scale sets 0 then 1
+    main_block(0, 2 * kb, sa0, sb0, sa1, sb1);
+    main_block(2, 2 * kb + 2, sa1, sb1, sa0, sb0);
   }
-  // ---- drain: the last (up to) two K blocks, no further loads
+
+  // ---- drain: the last (up to) two K blocks, no further loads.
   if (nkb >= 2) {
-    const int st = nst - 4;
-    wait_vm_barrier<W2>();  // younger than st+1: stages st+2 (even), st+3
-    read_frags(st + 1, fa1, fb1);
-    mfmas(fa0, fb0);
+    const int st = nst - 4;  // in slot 0, scale set 0
+    wait_vm_barrier<W2>();   // younger than st+1: stages st+2 (even), st+3
+    stage(0, st, false, true, false, fa0, fb0, fa1, fb1, sa0, sb0, sa1, sb1);
     wait_vm_barrier<LOADS>();  // younger than st+2: stage st+3
-    read_frags(st + 2, fa0, fb0);
-    read_scales(st + 2, sa_nxt, sb_nxt);
-    mfmas(fa1, fb1);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) sa_cur[mt] = sa_nxt[mt];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sb_cur[nt] = sb_nxt[nt];
-  }
-  if (nkb >= 1) {
-    const int st = nst - 2;
+    stage(1, st + 1, false, true, true, fa1, fb1, fa0, fb0, sa0, sb0, sa1, sb1);
     wait_vm_barrier<0>();
-    read_frags(st + 1, fa1, fb1);
-    mfmas(fa0, fb0);
-    mfmas(fa1, fb1);
+    stage(2, st + 2, false, true, false, fa0, fb0, fa1, fb1, sa1, sb1, sa0, sb0);
+    stage(3, st + 3, false, false, false, fa1, fb1, fa0, fb0, sa1, sb1, sa0, sb0);
+    mfma_retire_pad();
+  } else if (BM < 256 && nkb == 1) {  // the 256-wide tile is launched with K >= 256 only
+    wait_vm_barrier<0>();
+    stage(0, 0, false, true, false, fa0, fb0, fa1, fb1, sa0, sb0, sa1, sb1);
+    stage(1, 1, false, false, false, fa1, fb1, fa0, fb0, sa0, sb0, sa1, sb1);
+    mfma_retire_pad();
   }
 
   // ---- epilogue: lane holds C[m][nb .. nb+3] for nb = tile col + 8q + 4*(lane>>5)
@@ -399,7 +533,9 @@ void launch_shape(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda
                   const uint8_t* b, int64_t ldb, const uint8_t* sb, void* c, int64_t ldc, int c_dtype,
                   hipStream_t stream) {
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  const bool big = MXFP8_GEMM_TILE == 256 || (MXFP8_GEMM_TILE == 0 && big_tiles >= 256);
+  // The 256-wide tile needs K >= 256: a separate single-K-block drain would
+  // make the accumulators spill (merging three exit paths of 256 of them).
+  const bool big = K >= 256 && (MXFP8_GEMM_TILE == 256 || (MXFP8_GEMM_TILE == 0 && big_tiles >= 256));
   if (big)
     launch_tile<256, 256, 4, AFMT, BFMT, BKN, BROW>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
   else
