@@ -454,60 +454,123 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
     main_block(2, 2 * kb + 2, sa1, sb1, sa0, sb0);
   }
 
-  // ---- drain: the last (up to) two K blocks, no further loads.
+  // Pins the accumulators to AGPRs where the K loop ends: left free, the
+  // allocator moves some of them into VGPRs during the drain (the epilogue
+  // reads them through VALU) and spills fragments to make room.
+  auto pin_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+a"(acc[mt][nt]));
+  };
+
+  // ---- epilogue.  Lane l holds, for each (mt, nt), C[r][c .. c+3] with
+  // r = l & 31 and c = 8q + 4(l >> 5) (q = 0..3) inside the 32x32 block.
+  // Stored from registers directly, that is 16 rows x 16 bytes per store
+  // instruction.  Instead each wave stages one 32-row strip of its
+  // sub-tile at a time in LDS and writes it back row by row: every store
+  // instruction then covers whole 256-byte row segments.  The staging sits
+  // in two ring slots nothing reads any more (waves 0, 1 in the first, 2, 3
+  // in the second); only the wave itself touches its region, and LDS
+  // executes one wave's accesses in order, so no barrier is needed.
+  auto epilogue = [&](uint8_t* lo, uint8_t* hi) __attribute__((always_inline)) {
+    if (!out_bf16) {
+      constexpr int P = WN * 4 + 16;  // bytes per staged row
+      static_assert(2 * 32 * P <= ST, "staging fits a slot");
+      uint8_t* stg = (wave < 2 ? lo : hi) + (wave & 1) * (32 * P);
+      constexpr int CH = WN / 4;            // 16-byte chunks per row
+      constexpr int ROWS_PER = 64 / CH;     // rows per store instruction
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        __builtin_amdgcn_sched_barrier(0);  // one strip's accumulators at a time
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const v4f v = v4f{acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2],
+                              acc[mt][nt][4 * q + 3]};
+            *reinterpret_cast<v4f*>(stg + (lane & 31) * P + (nt * 32 + 8 * q + 4 * g) * 4) = v;
+          }
+        const int row0 = m0 + wm * WM + mt * 32;
+#pragma unroll
+        for (int it = 0; it < 32 / ROWS_PER; ++it) {
+          const int rr = it * ROWS_PER + lane / CH, ch = lane % CH;
+          const v4f v = *reinterpret_cast<const v4f*>(stg + rr * P + ch * 16);
+          const int m = row0 + rr, n = n0 + wn * WN + ch * 4;
+          if (m < M) {
+            float* dst = reinterpret_cast<float*>(C) + (int64_t)m * ldc + n;
+            if (n + 3 < N) {
+              *reinterpret_cast<v4f*>(dst) = v;
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (n + i < N) dst[i] = v[i];
+            }
+          }
+        }
+      }
+    } else {
+      constexpr int P = WN * 2 + 16;
+      uint8_t* stg = (wave < 2 ? lo : hi) + (wave & 1) * (32 * P);
+      constexpr int CH = WN / 8;
+      constexpr int ROWS_PER = 64 / CH;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        __builtin_amdgcn_sched_barrier(0);  // one strip's accumulators at a time
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint2 o;
+            o.x = bf16_rne(acc[mt][nt][4 * q]) | (bf16_rne(acc[mt][nt][4 * q + 1]) << 16);
+            o.y = bf16_rne(acc[mt][nt][4 * q + 2]) | (bf16_rne(acc[mt][nt][4 * q + 3]) << 16);
+            *reinterpret_cast<uint2*>(stg + (lane & 31) * P + (nt * 32 + 8 * q + 4 * g) * 2) = o;
+          }
+        const int row0 = m0 + wm * WM + mt * 32;
+#pragma unroll
+        for (int it = 0; it < 32 / ROWS_PER; ++it) {
+          const int rr = it * ROWS_PER + lane / CH, ch = lane % CH;
+          const uint4 v = *reinterpret_cast<const uint4*>(stg + rr * P + ch * 16);
+          const int m = row0 + rr, n = n0 + wn * WN + ch * 8;
+          if (m < M) {
+            uint16_t* dst = reinterpret_cast<uint16_t*>(C) + (int64_t)m * ldc + n;
+            if (n + 7 < N) {
+              *reinterpret_cast<uint4*>(dst) = v;
+            } else {
+              const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+              for (int i = 0; i < 8; ++i)
+                if (n + i < N) dst[i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+            }
+          }
+        }
+      }
+    }
+  };
+
+  // ---- drain: the last (up to) two K blocks, no further loads; then the
+  // epilogue.  Each exit path ends in its own epilogue.
   if (nkb >= 2) {
     const int st = nst - 4;  // in slot 0, scale set 0
     wait_vm_barrier<W2>();   // younger than st+1: stages st+2 (even), st+3
     stage(0, st, false, true, false, fa0, fb0, fa1, fb1, sa0, sb0, sa1, sb1);
     wait_vm_barrier<LOADS>();  // younger than st+2: stage st+3
     stage(1, st + 1, false, true, true, fa1, fb1, fa0, fb0, sa0, sb0, sa1, sb1);
-    wait_vm_barrier<0>();
+    wait_vm_barrier<0>();  // after it no wave reads slots 0..2 again
     stage(2, st + 2, false, true, false, fa0, fb0, fa1, fb1, sa1, sb1, sa0, sb0);
     stage(3, st + 3, false, false, false, fa1, fb1, fa0, fb0, sa1, sb1, sa0, sb0);
     mfma_retire_pad();
+    pin_acc();
+    epilogue(ring0, ring1);
   } else if (BM < 256 && nkb == 1) {  // the 256-wide tile is launched with K >= 256 only
     wait_vm_barrier<0>();
     stage(0, 0, false, true, false, fa0, fb0, fa1, fb1, sa0, sb0, sa1, sb1);
     stage(1, 1, false, false, false, fa1, fb1, fa0, fb0, sa0, sb0, sa1, sb1);
     mfma_retire_pad();
-  }
-
-  // ---- epilogue: lane holds C[m][nb .. nb+3] for nb = tile col + 8q + 4*(lane>>5)
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = m0 + wm * WM + mt * 32 + (lane & 31);
-    if (m >= M) continue;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nb = n0 + wn * WN + nt * 32 + 8 * q + 4 * g;
-        const v4f v = v4f{acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2],
-                          acc[mt][nt][4 * q + 3]};
-        if (!out_bf16) {
-          float* crow = reinterpret_cast<float*>(C) + (int64_t)m * ldc;
-          if (nb + 3 < N) {
-            *reinterpret_cast<v4f*>(crow + nb) = v;
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (nb + i < N) crow[nb + i] = v[i];
-          }
-        } else {
-          uint16_t* crow = reinterpret_cast<uint16_t*>(C) + (int64_t)m * ldc;
-          if (nb + 3 < N) {
-            uint2 o;
-            o.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-            o.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-            *reinterpret_cast<uint2*>(crow + nb) = o;
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (nb + i < N) crow[nb + i] = (uint16_t)bf16_rne(v[i]);
-          }
-        }
-      }
-    }
+    pin_acc();
+    epilogue(ring2, ring3);  // never loaded when K = 128
+  } else if (BM < 256) {
+    epilogue(ring0, ring1);  // K = 0: zeros
   }
 #endif
 }
