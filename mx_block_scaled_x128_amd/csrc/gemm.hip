@@ -49,7 +49,6 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
 constexpr int kThreads = 256;  // 4 waves, arranged 2 x 2 over the tile
-constexpr int BK = 64;         // K per pipeline stage
 
 __device__ __forceinline__ uint32_t bf16_rne(float v) {
   uint32_t b = __float_as_uint(v);
@@ -57,10 +56,10 @@ __device__ __forceinline__ uint32_t bf16_rne(float v) {
   return b >> 16;
 }
 
-// [rows][64 B] stage tiles: row r, logical 16-byte chunk c at physical chunk
-// c ^ ((r >> 2) & 3); sixteen consecutive rows read at one logical chunk hit
-// 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
+// [rows][128 B] K-block tiles: row r, logical 16-byte chunk c at physical
+// chunk c ^ ((r >> 1) & 7); sixteen consecutive rows read at one logical
+// chunk hit 16 distinct 16-byte bank groups (two rows span all 64 banks).
+__device__ __forceinline__ int swz128(int r) { return (r >> 1) & 7; }
 
 // [64 k][BN bytes] stage tiles of B stored [K][N] (CPR = BN / 16 chunks per
 // row): chunk c of row k at physical chunk c ^ s(k), s(k) even, so the two
@@ -129,72 +128,84 @@ __device__ __forceinline__ void mfma_retire_pad() {
 #endif
 }
 
-// MFMAs a stage issues before its first LDS read or HBM->LDS load.
-#ifndef MXFP8_GEMM_LEAD
-#define MXFP8_GEMM_LEAD 0
+// Fraction (in quarters) of a stage's MFMAs over which the next stage's
+// fragment reads are spread.
+#ifndef MXFP8_GEMM_DS_SPAN
+#define MXFP8_GEMM_DS_SPAN 3
 #endif
 
 template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ SA,
     const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ SB, void* __restrict__ C,
-    int64_t ldc, int out_bf16, int tiles_m, int tiles_n) {
+    int64_t ldc, int out_bf16, int tiles_m, int tiles_n, int tile_first, int split) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int MT = WM / 32, NT = WN / 32;          // 32x32 MFMA tiles per wave
-  // Ring slot: A tile [BM][64 B], B tile, then (used by even stages) one
-  // dword per row of A and per column of B holding that K block's scale byte.
-  constexpr int A_ST = BM * BK, B_ST = BN * BK;
-  constexpr int SA_OFF = A_ST + B_ST, SB_OFF = SA_OFF + kThreads * 4, ST = SB_OFF + kThreads * 4;
-  constexpr int A_LOADS = A_ST / (kThreads * 16), B_LOADS = B_ST / (kThreads * 16);
-  constexpr int LOADS = A_LOADS + B_LOADS;           // tile VMEM instructions per stage per thread
-  constexpr int SLOADS = 2;                          // scale VMEM instructions per K block
+  // LDS: two K-block buffers, each holding both 64-wide stages of one
+  // 128-wide K block: the A tile [BM][128 B], the B tile ([BN][128 B], or
+  // [128 k][BN B] when B is [K][N]), then one dword per row of A and per
+  // column of B holding that K block's scale byte.  Whole 128-byte rows per
+  // load instruction: HBM/L2 lines are 128 bytes, and loading a row's two
+  // 64-byte halves in different stages fetched every line twice.
+  constexpr int KBB = 128;                           // K bytes per buffer row
+  constexpr int A_ST = BM * KBB, B_ST = BN * KBB;
+  constexpr int SA_OFF = A_ST + B_ST, SB_OFF = SA_OFF + kThreads * 4, PB = SB_OFF + kThreads * 4;
+  constexpr int A_LOADS = A_ST / (kThreads * 16), B_LOADS = B_ST / (kThreads * 16);  // per K block, per thread
+  constexpr int SLOADS = 2;                          // scale loads per K block, per thread
   constexpr int CPR = BN / 16;
   static_assert(BM % 64 == 0 && BN % 64 == 0 && A_LOADS >= 1 && B_LOADS >= 1, "tile");
   static_assert(BM <= kThreads && BN <= kThreads, "one scale slot per thread");
-  static_assert(3 * LOADS + 2 * SLOADS <= 63, "vmcnt range");
+  static_assert(A_LOADS + B_LOADS + SLOADS <= 63, "vmcnt range");
+  (void)STAGES;
 
-  // The LDS ring: one array per slot.  Every access names its slot with a
-  // compile-time constant (the loops below are unrolled so that it does), so
-  // the compiler can tell slots apart: it then does not drain in-flight
-  // LDS-bound loads before reading a different slot (it must assume that a
-  // read may alias an in-flight load into the same array).
-  static_assert(STAGES == 4, "four ring slots");
-  __shared__ __attribute__((aligned(1024))) uint8_t ring0[ST];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring1[ST];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring2[ST];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring3[ST];
-  auto slot_ptr = [&](int sl) __attribute__((always_inline)) -> uint8_t* { return sl == 0 ? ring0 : sl == 1 ? ring1 : sl == 2 ? ring2 : ring3; };
+  // One array per buffer; every access names its buffer with a compile-time
+  // constant (the loops below are unrolled so that it does), so the compiler
+  // can tell the buffers apart and does not drain in-flight LDS-bound loads
+  // into one buffer before reading the other.
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[PB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[PB];
+  auto buf_ptr = [&](int p) __attribute__((always_inline)) -> uint8_t* { return p == 0 ? kbuf0 : kbuf1; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // known uniform: LDS destinations stay scalar
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- tile of this workgroup
+  // ---- tile of this workgroup.  Tiles are enumerated over a grid of
+  // tiles_m x tiles_n cells of (BM << split) x (BN << split), in groups of
+  // GROUP cell rows walked column by column; this launch covers cells
+  // tile_first, tile_first + 1, ... and, with split = 1, each cell as four
+  // BM x BN quadrants (one workgroup each).  Workgroup ids are first
+  // remapped so that each XCD (ids are dealt round-robin to the 8 XCDs)
+  // walks a contiguous band of that order.
   int wg = blockIdx.x;
-  const int nwg = tiles_m * tiles_n;
+  const int nwg = gridDim.x;
   if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
+  const int cell = tile_first + (wg >> (2 * split));
+  const int quad = wg & ((1 << (2 * split)) - 1);
   constexpr int GROUP = 8;
-  const int group = wg / (GROUP * tiles_n);
+  const int group = cell / (GROUP * tiles_n);
   const int first = group * GROUP;
   const int gsz = min(tiles_m - first, GROUP);
-  const int within = wg - group * GROUP * tiles_n;
-  const int m0 = (first + within % gsz) * BM;
-  const int n0 = (within / gsz) * BN;
+  const int within = cell - group * GROUP * tiles_n;
+  const int m0 = (((first + within % gsz) << split) + (quad >> split)) * BM;
+  const int n0 = (((within / gsz) << split) + (quad & split)) * BN;
+  if (m0 >= M || n0 >= N) return;  // a quadrant past the matrix edge (uniform per workgroup)
 
-  const int nst = K / BK;   // stages (even: K % 128 == 0)
-  const int nkb = K >> 7;   // 128-wide scale blocks
+  const int nkb = K >> 7;   // 128-wide K blocks (= scale blocks)
   const int nnb = (N + 127) >> 7;
 
   // ---- HBM -> LDS sources: uniform tile bases + per-lane 32-bit offsets.
-  // Each wave-instruction fills 1 KB of LDS in lane order; the offsets encode
-  // the row swizzle.  Rows past M / N are clamped (their results are dropped).
+  // Each wave-instruction fills 1 KB of LDS in lane order: 8 rows of 128
+  // bytes (lane l: row l >> 3, physical chunk l & 7, which holds logical
+  // chunk (l & 7) ^ swz128(row)).  Rows past M / N are clamped (their results
+  // are dropped).
   const uint8_t* a_base = A + (int64_t)m0 * lda;
   uint32_t a_off[A_LOADS];
 #pragma unroll
   for (int j = 0; j < A_LOADS; ++j) {
-    const int row = (j * 4 + wave) * 16 + (lane >> 2);
-    const int lc = (lane & 3) ^ swz64(row);
+    const int row = (j * 4 + wave) * 8 + (lane >> 3);
+    const int lc = (lane & 7) ^ swz128(row);
     a_off[j] = (uint32_t)((min(m0 + row, M - 1) - m0) * lda + lc * 16);
   }
   const uint8_t* b_base = BKN ? B : B + (int64_t)n0 * ldb;
@@ -202,8 +213,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
 #pragma unroll
   for (int j = 0; j < B_LOADS; ++j) {
     if (!BKN) {
-      const int row = (j * 4 + wave) * 16 + (lane >> 2);
-      const int lc = (lane & 3) ^ swz64(row);
+      const int row = (j * 4 + wave) * 8 + (lane >> 3);
+      const int lc = (lane & 7) ^ swz128(row);
       b_off[j] = (uint32_t)((min(n0 + row, N - 1) - n0) * ldb + lc * 16);
     } else {
       constexpr int RPI = 64 / CPR;  // k rows per wave-instruction
@@ -214,11 +225,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
       b_off[j] = (uint32_t)(krow * ldb + col);
     }
   }
-  const int64_t b_step = BKN ? (int64_t)BK * ldb : BK;
+  const int64_t b_step = BKN ? (int64_t)KBB * ldb : KBB;
 
   // Scale sources: thread t fetches the scale byte of tile row t (A) and of
   // tile column t (B) for a K block; the byte lands zero-extended in dword t
-  // of the slot's scale area (the LDS layout of 1-byte LDS-bound loads).
+  // of the buffer's scale area (the LDS layout of 1-byte LDS-bound loads).
   const uint8_t* sa_base = SA + (int64_t)m0 * nkb;
   const uint32_t sa_off = (uint32_t)((min(m0 + tid, M - 1) - m0) * nkb);
   const uint8_t* sb_base;
@@ -235,52 +246,50 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
     sb_step = BKN ? nnb : 1;
   }
 
-  // LDS-bound loads of stage st into ring slot sl (= st % STAGES), one
-  // instruction per item: items 0..SLOADS-1 are the scale bytes (even stages
-  // only), then A_LOADS tile loads of A and B_LOADS of B.
+  // LDS-bound loads of K block kb into buffer p, one instruction per item:
+  // items 0..SLOADS-1 are the scale bytes, then A_LOADS loads of A and
+  // B_LOADS of B.
   constexpr int DMA_ITEMS = SLOADS + A_LOADS + B_LOADS;
   struct Src {
     const uint8_t *a, *b, *sa, *sb;
   };
-  auto dma_src = [&](int st) __attribute__((always_inline)) {
-    const int kb = st >> 1;
+  auto dma_src = [&](int kb) __attribute__((always_inline)) {
     Src src;
-    src.a = uniform_opaque(a_base + (int64_t)st * BK);
-    src.b = uniform_opaque(b_base + (int64_t)st * b_step);
+    src.a = uniform_opaque(a_base + (int64_t)kb * KBB);
+    src.b = uniform_opaque(b_base + (int64_t)kb * b_step);
     src.sa = uniform_opaque(sa_base + kb);
     src.sb = uniform_opaque(sb_base + (int64_t)kb * sb_step);
     return src;
   };
-  auto dma_item = [&](int sl, const Src& src, int item) __attribute__((always_inline)) {
-    uint8_t* slot = slot_ptr(sl);
+  auto dma_item = [&](int p, const Src& src, int item) __attribute__((always_inline)) {
+    uint8_t* buf = buf_ptr(p);
     if (item == 0) {
-      __builtin_amdgcn_global_load_lds(src.sa + sa_off, slot + SA_OFF + wave * 256, 1, 0, 0);
+      __builtin_amdgcn_global_load_lds(src.sa + sa_off, buf + SA_OFF + wave * 256, 1, 0, 0);
     } else if (item == 1) {
-      __builtin_amdgcn_global_load_lds(src.sb + sb_off, slot + SB_OFF + wave * 256, 1, 0, 0);
+      __builtin_amdgcn_global_load_lds(src.sb + sb_off, buf + SB_OFF + wave * 256, 1, 0, 0);
     } else if (item < SLOADS + A_LOADS) {
       const int j = item - SLOADS;
-      __builtin_amdgcn_global_load_lds(src.a + a_off[j], slot + (j * 4 + wave) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src.a + a_off[j], buf + (j * 4 + wave) * 1024, 16, 0, 0);
     } else {
       const int j = item - SLOADS - A_LOADS;
-      __builtin_amdgcn_global_load_lds(src.b + b_off[j], slot + A_ST + (j * 4 + wave) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src.b + b_off[j], buf + A_ST + (j * 4 + wave) * 1024, 16, 0, 0);
     }
   };
-  auto dma = [&](int sl, int st) __attribute__((always_inline)) {
-    const Src src = dma_src(st);
+  auto dma_kblock = [&](int p, int kb) __attribute__((always_inline)) {
+    const Src src = dma_src(kb);
 #pragma unroll
-    for (int item = 0; item < DMA_ITEMS; ++item)
-      if (item >= SLOADS || (st & 1) == 0) dma_item(sl, src, item);
+    for (int item = 0; item < DMA_ITEMS; ++item) dma_item(p, src, item);
   };
 
-  // Scale operands of the K block whose even stage sits in slot sl.
+  // Scale operands of the K block in buffer p.
   const uint32_t sa_rd = opaque(SA_OFF + (wm * WM + (lane & 31)) * 4);
   const uint32_t sb_rd = opaque(SB_OFF + (wn * WN + (lane & 31)) * 4);
-  auto read_scales = [&](int sl, int (&sa)[MT], int (&sb)[NT]) __attribute__((always_inline)) {
-    const uint8_t* slot = slot_ptr(sl);
+  auto read_scales = [&](int p, int (&sa)[MT], int (&sb)[NT]) __attribute__((always_inline)) {
+    const uint8_t* buf = buf_ptr(p);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) sa[mt] = *reinterpret_cast<const int*>(slot + sa_rd + mt * 128);
+    for (int mt = 0; mt < MT; ++mt) sa[mt] = *reinterpret_cast<const int*>(buf + sa_rd + mt * 128);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sb[nt] = *reinterpret_cast<const int*>(slot + sb_rd + nt * 128);
+    for (int nt = 0; nt < NT; ++nt) sb[nt] = *reinterpret_cast<const int*>(buf + sb_rd + nt * 128);
   };
 
   v16f acc[MT][NT];
@@ -292,108 +301,103 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
       for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.0f;
 
   const int g = lane >> 5;
-  // Fragments of one stage from its LDS buffer.  Lane l holds, for its row
-  // (A) / column (B) l & 31, bytes k = 32*(l>>5) .. +31 of the 64-wide stage,
+  // Fragments of one 64-wide stage (half h of a K block).  Lane l holds, for
+  // its row (A) / column (B) l & 31, bytes k = 32*(l>>5) .. +31 of the stage,
   // in k order, for both operands (the pairing the MFMA needs).  One LDS read
-  // per item: A items 2*mt + half (16 bytes each), then B items (two 16-byte
-  // halves per fragment, or four 8-byte transposed parts when B is [K][N]).
+  // per item: A items 2*mt + part (16 bytes each), then B items (two 16-byte
+  // parts per fragment, or four 8-byte transposed parts when B is [K][N]).
   constexpr int B_PARTS = BKN ? 4 : 2;
   constexpr int DS_ITEMS = 2 * MT + B_PARTS * NT;
-  // Per-lane read offsets within a slot (the 32-row / 32-column step of a
-  // fragment and the 8-row step of a transposed part are added as constants:
-  // neither changes the swizzle, which depends only on low row bits).
-  uint32_t a_rd[2], b_rd[BKN ? NT : 2];
+  // Per-lane read offsets within a buffer, per stage half (the 32-row /
+  // 32-column step of a fragment and the 8-row step of a transposed part are
+  // added as constants: neither changes the swizzle, which depends only on
+  // low row bits).
+  uint32_t a_rd[2][2], b_rd[2][BKN ? NT : 2];
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int r = wm * WM + (lane & 31);
-    a_rd[half] = opaque(r * 64 + (((2 * g + half) ^ swz64(r)) << 4));
-  }
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+      const int r = wm * WM + (lane & 31);
+      a_rd[h][part] = opaque(r * KBB + (((4 * h + 2 * g + part) ^ swz128(r)) << 4));
+    }
   if (!BKN) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int r = wn * WN + (lane & 31);
-      b_rd[half] = opaque(A_ST + r * 64 + (((2 * g + half) ^ swz64(r)) << 4));
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        const int r = wn * WN + (lane & 31);
+        b_rd[h][part] = opaque(A_ST + r * KBB + (((4 * h + 2 * g + part) ^ swz128(r)) << 4));
+      }
   } else {
     // 16-lane group grp covers columns 16*(grp&1) .. +15 and k half grp>>1;
     // lane pair (2j, 2j+1) points at row k of that block, bytes 0-7 / 8-15.
     const int grp = lane >> 4, j = (lane & 15) >> 1, half = lane & 1;
-    const int k = 32 * (grp >> 1) + j;
 #pragma unroll
-    for (int nt = 0; nt < (BKN ? NT : 0); ++nt) {
-      const int nsub = ((wn * WN + nt * 32) >> 4) + (grp & 1);
-      b_rd[nt] = opaque(A_ST + k * BN + ((nsub ^ swz_kn<CPR>(k)) << 4) + half * 8);
+    for (int h = 0; h < 2; ++h) {
+      const int k = 64 * h + 32 * (grp >> 1) + j;
+#pragma unroll
+      for (int nt = 0; nt < (BKN ? NT : 0); ++nt) {
+        const int nsub = ((wn * WN + nt * 32) >> 4) + (grp & 1);
+        b_rd[h][nt] = opaque(A_ST + k * BN + ((nsub ^ swz_kn<CPR>(k)) << 4) + half * 8);
+      }
     }
   }
-  auto ds_item = [&](int sl, int item, v8i (&af)[MT], v8i (&bfr)[NT]) __attribute__((always_inline)) {
-    const uint8_t* lds = slot_ptr(sl);
+  auto ds_item = [&](int p, int h, int item, v8i (&af)[MT], v8i (&bfr)[NT]) __attribute__((always_inline)) {
+    const uint8_t* buf = buf_ptr(p);
     if (item < 2 * MT) {
-      const int mt = item >> 1, half = item & 1;
-      const v4i v = *reinterpret_cast<const v4i*>(lds + a_rd[half] + mt * 2048);
-      if (half == 0) af[mt].s0123 = v;
+      const int mt = item >> 1, part = item & 1;
+      const v4i v = *reinterpret_cast<const v4i*>(buf + a_rd[h][part] + mt * 32 * KBB);
+      if (part == 0) af[mt].s0123 = v;
       else af[mt].s4567 = v;
     } else if (!BKN) {
-      const int nt = (item - 2 * MT) >> 1, half = item & 1;
-      const v4i v = *reinterpret_cast<const v4i*>(lds + b_rd[half] + nt * 2048);
-      if (half == 0) bfr[nt].s0123 = v;
+      const int nt = (item - 2 * MT) >> 1, part = item & 1;
+      const v4i v = *reinterpret_cast<const v4i*>(buf + b_rd[h][part] + nt * 32 * KBB);
+      if (part == 0) bfr[nt].s0123 = v;
       else bfr[nt].s4567 = v;
     } else {
       // part t: k rows 8t .. 8t+7 of the lane's k half
       const int nt = (item - 2 * MT) >> 2, t = (item - 2 * MT) & 3;
-      const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(lds + b_rd[nt] + 8 * t * BN));
+      const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(buf + b_rd[h][nt] + 8 * t * BN));
       if (t == 0) bfr[nt].s01 = v;
       else if (t == 1) bfr[nt].s23 = v;
       else if (t == 2) bfr[nt].s45 = v;
       else bfr[nt].s67 = v;
     }
   };
-  auto read_frags = [&](int sl, v8i (&af)[MT], v8i (&bfr)[NT]) __attribute__((always_inline)) {
+  auto read_frags = [&](int p, int h, v8i (&af)[MT], v8i (&bfr)[NT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int item = 0; item < DS_ITEMS; ++item) ds_item(sl, item, af, bfr);
+    for (int item = 0; item < DS_ITEMS; ++item) ds_item(p, h, item, af, bfr);
   };
 
-  // One stage as an explicit instruction stream.  The first LEAD MFMAs go
-  // out alone; after that each MFMA is followed by its share of the next
-  // stage's LDS reads (all within the first half of the remaining steps, so
-  // they land well before the next barrier) and of the HBM->LDS loads, spread
-  // evenly (one per MFMA on the 256-wide tile: a burst would stall this
-  // wave's in-order issue and starve its MFMA pipe).  sched_barrier(0) keeps
-  // the order.
+  // One stage as an explicit instruction stream: MFMA i, then the LDS reads
+  // and HBM->LDS loads whose turn comes after it.  The loads are spread
+  // evenly over the whole stage and the next stage's fragment reads over its
+  // first DS_SPAN MFMAs: an LDS-bound load stalls this wave's in-order issue
+  // whenever the CU's load path is busy, and a burst of them starves the
+  // MFMA pipe.  sched_barrier(0) keeps the order.
   constexpr int MFMAS = MT * NT;
-  constexpr int LEAD = MXFP8_GEMM_LEAD;
-  constexpr int STEPS = MFMAS - LEAD;
-  static_assert(STEPS >= 2, "tile");
-  constexpr int DS_PER_STEP = (DS_ITEMS + STEPS / 2 - 1) / (STEPS / 2);
-  constexpr int DMA_PER_STEP = (DMA_ITEMS + STEPS - 1) / STEPS;
-  // Stage st lives in slot sl and multiplies with the scales (csa, csb).
-  // do_dma: refill slot sl with stage st + STAGES (same parity as st).
-  // do_ds: read stage st+1's fragments from the next slot into (na, nb).
-  // do_sc: also read the scales stored with stage st+1 (an even stage: a new
-  // K block) into (nsa, nsb).
-  auto stage = [&](int sl, int st, bool do_dma, bool do_ds, bool do_sc, const v8i (&ca)[MT],
+  constexpr int DS_SPAN = MFMAS * MXFP8_GEMM_DS_SPAN / 4 > 0 ? MFMAS * MXFP8_GEMM_DS_SPAN / 4 : 1;
+  // The stage multiplies fragments (ca, cb) with scales (csa, csb).
+  // dma_p >= 0: load K block dma_kb into buffer dma_p meanwhile.
+  // rd_p >= 0: read the fragments of stage half rd_h of buffer rd_p into
+  // (na, nb); with do_sc also that buffer's scales into (nsa, nsb).
+  auto stage = [&](int dma_p, int dma_kb, int rd_p, int rd_h, bool do_sc, const v8i (&ca)[MT],
                    const v8i (&cb)[NT], v8i (&na)[MT], v8i (&nb)[NT], const int (&csa)[MT],
                    const int (&csb)[NT], int (&nsa)[MT], int (&nsb)[NT]) __attribute__((always_inline)) {
-    const bool even_dma = (st & 1) == 0;
-    const Src src = dma_src(st + STAGES);
+    Src src = {nullptr, nullptr, nullptr, nullptr};
+    if (dma_p >= 0) src = dma_src(dma_kb);
 #pragma unroll
     for (int i = 0; i < MFMAS; ++i) {
       const int mt = i / NT, nt = i % NT;
       acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[nt], ca[mt], acc[mt][nt], BFMT, AFMT, 0,
                                                                    csb[nt], 0, csa[mt]);
-      if (i >= LEAD) {
-        const int j = i - LEAD;
-        if (do_sc && j == 0) read_scales((sl + 1) & 3, nsa, nsb);
+      if (rd_p >= 0 && do_sc && i == 0) read_scales(rd_p, nsa, nsb);
 #pragma unroll
-        for (int d = 0; d < DS_PER_STEP; ++d) {
-          const int item = j * DS_PER_STEP + d;
-          if (do_ds && item < DS_ITEMS) ds_item((sl + 1) & 3, item, na, nb);
-        }
+      for (int item = 0; item < DS_ITEMS; ++item)
+        if (rd_p >= 0 && item * DS_SPAN / DS_ITEMS == i) ds_item(rd_p, rd_h, item, na, nb);
 #pragma unroll
-        for (int d = 0; d < DMA_PER_STEP; ++d) {
-          const int item = j * DMA_PER_STEP + d;
-          if (do_dma && item < DMA_ITEMS && (item >= SLOADS || even_dma)) dma_item(sl, src, item);
-        }
-      }
+      for (int item = 0; item < DMA_ITEMS; ++item)
+        if (dma_p >= 0 && item * MFMAS / DMA_ITEMS == i) dma_item(dma_p, src, item);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -403,55 +407,54 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   v8i fa0[MT], fb0[NT], fa1[MT], fb1[NT];
   int sa0[MT], sb0[NT], sa1[MT], sb1[NT];
 
-  // Slots: stage st sits in slot (st + s0) % 4.  s0 is chosen so that the
-  // drain (the last two K blocks) always starts in slot 0; every loop body
-  // below then names its slots as constants.
-  constexpr int W2 = LOADS * 2 + SLOADS;
-  const int main_kb = nkb - 2;  // K blocks whose stages all refill the ring
-  const bool odd_main = main_kb > 0 && (main_kb & 1);
-
-  // ---- prologue: STAGES stages of loads in flight (scale bytes ride with
-  // the even stages), then stage 0's fragments and K block 0's scales (into
-  // the set the first block uses: set 1 when a lone main block precedes the
-  // paired loop, else set 0).
-  auto prologue = [&](int s0, int (&psa)[MT], int (&psb)[NT]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < STAGES; ++i)
-      if (i < nst) dma((s0 + i) & 3, i);
-    // younger than stage 0: stages 1..3 = 3 tile batches + one scale batch (stage 2)
-    if (nst >= 4) wait_vm_barrier<LOADS * 3 + SLOADS>();
-    else wait_vm_barrier<LOADS>();  // nst == 2: only stage 1 is younger
-    read_frags(s0, fa0, fb0);
-    read_scales(s0, psa, psb);
+  // ---- schedule.  Each K block's first stage
+  // multiplies while the second stage's fragments are read.  At the top of
+  // its second stage every wave waits for all its loads (K block kb+1,
+  // issued one K block earlier) and meets the others: K block kb+1 has then
+  // landed everywhere, and nobody reads kb's buffer any more, so the second
+  // stage refills it with K block kb+2 while reading K block kb+1's first
+  // fragments and scales.  One barrier per K block.
+  // kblock(p, kb, ...): K block kb in buffer p with scale set (csa, csb);
+  // dma: load K block kb+2; next: kb+1 exists (read its scales into (nsa, nsb)).
+  auto kblock = [&](int p, int kb, bool dma, bool next, const int (&csa)[MT], const int (&csb)[NT],
+                    int (&nsa)[MT], int (&nsb)[NT]) __attribute__((always_inline)) {
+    stage(-1, 0, p, 1, false, fa0, fb0, fa1, fb1, csa, csb, nsa, nsb);
+    if (dma || next) wait_vm_barrier<0>();
+    stage(dma ? p : -1, kb + 2, next ? (p ^ 1) : -1, 0, next, fa1, fb1, fa0, fb0, csa, csb, nsa, nsb);
   };
-  if (nst > 0) {
-    if (odd_main) prologue(2, sa1, sb1);
-    else prologue(0, sa0, sb0);
+
+  // ---- prologue: K blocks 0 and 1 in flight, then K block 0's first
+  // fragments and scales.  K block kb sits in buffer kb % 2.
+  if (nkb > 0) {
+    dma_kblock(0, 0);
+    if (nkb > 1) {
+      dma_kblock(1, 1);
+      wait_vm_barrier<DMA_ITEMS>();
+    } else {
+      wait_vm_barrier<0>();
+    }
+    read_frags(0, 0, fa0, fb0);
+    read_scales(0, sa0, sb0);
   }
 
-  // ---- steady state.  At the top of stage st: (1) stage st+1 has landed for
-  // every wave and every wave holds stage st's fragments, so (2) stage st's
-  // slot is refilled with stage st + STAGES; (3) stage st's MFMAs run while
-  // stage st+1's fragments (and, for an even st+1, its K block's scales) are
-  // read.  Two younger stages, one of them even, are in flight at each wait.
-  // One K block = two stages starting at an even stage in slot sl (0 or 2),
-  // using scale set (csa, csb) and loading the next block's into (nsa, nsb).
-  auto main_block = [&](int sl, int st, const int (&csa)[MT], const int (&csb)[NT], int (&nsa)[MT],
-                        int (&nsb)[NT]) __attribute__((always_inline)) {
-    wait_vm_barrier<W2>();
-    stage(sl, st, true, true, false, fa0, fb0, fa1, fb1, csa, csb, nsa, nsb);
-    wait_vm_barrier<W2>();
-    stage(sl + 1, st + 1, true, true, true, fa1, fb1, fa0, fb0, csa, csb, nsa, nsb);
-  };
+  // ---- steady state: K blocks whose second stage loads a later block, in
+  // pairs, then a lone one if their count is odd.  The loop body names its
+  // buffers as constants and every path into the loop has the same loads in
+  // flight, so the compiler's per-buffer tracking of in-flight LDS-bound
+  // loads stays exact around it.
+  const int main_kb = nkb - 2;  // K blocks whose second stage loads a later block
   int kb = 0;
-  if (odd_main) {
-    main_block(2, 0, sa1, sb1, sa0, sb0);
-    kb = 1;
-  }
 #pragma nounroll
-  for (; kb < main_kb; kb += 2) {  // two K blocks: slots 0..3, scale sets 0 then 1
-    main_block(0, 2 * kb, sa0, sb0, sa1, sb1);
-    main_block(2, 2 * kb + 2, sa1, sb1, sa0, sb0);
+  for (; kb + 1 < main_kb; kb += 2) {  // two K blocks: buffers 0, 1; scale sets 0, 1
+    kblock(0, kb, true, true, sa0, sb0, sa1, sb1);
+    kblock(1, kb + 1, true, true, sa1, sb1, sa0, sb0);
+  }
+  if (kb < main_kb) {
+    kblock(0, kb, true, true, sa0, sb0, sa1, sb1);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) sa0[mt] = sa1[mt];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) sb0[nt] = sb1[nt];
   }
 
   // Pins the accumulators to AGPRs where the K loop ends: left free, the
@@ -473,11 +476,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // in two ring slots nothing reads any more (waves 0, 1 in the first, 2, 3
   // in the second); only the wave itself touches its region, and LDS
   // executes one wave's accesses in order, so no barrier is needed.
-  auto epilogue = [&](uint8_t* lo, uint8_t* hi) __attribute__((always_inline)) {
+  auto epilogue = [&](uint8_t* stage_buf) __attribute__((always_inline)) {
     if (!out_bf16) {
       constexpr int P = WN * 4 + 16;  // bytes per staged row
-      static_assert(2 * 32 * P <= ST, "staging fits a slot");
-      uint8_t* stg = (wave < 2 ? lo : hi) + (wave & 1) * (32 * P);
+      static_assert(4 * 32 * P <= PB, "staging fits a buffer");
+      uint8_t* stg = stage_buf + wave * (32 * P);
       constexpr int CH = WN / 4;            // 16-byte chunks per row
       constexpr int ROWS_PER = 64 / CH;     // rows per store instruction
 #pragma unroll
@@ -511,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
       }
     } else {
       constexpr int P = WN * 2 + 16;
-      uint8_t* stg = (wave < 2 ? lo : hi) + (wave & 1) * (32 * P);
+      uint8_t* stg = stage_buf + wave * (32 * P);
       constexpr int CH = WN / 8;
       constexpr int ROWS_PER = 64 / CH;
 #pragma unroll
@@ -549,28 +552,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   };
 
   // ---- drain: the last (up to) two K blocks, no further loads; then the
-  // epilogue.  Each exit path ends in its own epilogue.
+  // epilogue.  Their buffers depend on the parity of the K block count and
+  // are chosen at run time here (this costs a full wait for the last load
+  // before the drain's first LDS read, once per tile).  Each exit path has
+  // its own epilogue, in a buffer nobody reads after the drain's barrier.
   if (nkb >= 2) {
-    const int st = nst - 4;  // in slot 0, scale set 0
-    wait_vm_barrier<W2>();   // younger than st+1: stages st+2 (even), st+3
-    stage(0, st, false, true, false, fa0, fb0, fa1, fb1, sa0, sb0, sa1, sb1);
-    wait_vm_barrier<LOADS>();  // younger than st+2: stage st+3
-    stage(1, st + 1, false, true, true, fa1, fb1, fa0, fb0, sa0, sb0, sa1, sb1);
-    wait_vm_barrier<0>();  // after it no wave reads slots 0..2 again
-    stage(2, st + 2, false, true, false, fa0, fb0, fa1, fb1, sa1, sb1, sa0, sb0);
-    stage(3, st + 3, false, false, false, fa1, fb1, fa0, fb0, sa1, sb1, sa0, sb0);
+    const int p = nkb & 1;  // buffer of K block nkb - 2
+    kblock(p, nkb - 2, false, true, sa0, sb0, sa1, sb1);
+    kblock(p ^ 1, nkb - 1, false, false, sa1, sb1, sa0, sb0);
     mfma_retire_pad();
     pin_acc();
-    epilogue(ring0, ring1);
+    epilogue(buf_ptr(p));
   } else if (BM < 256 && nkb == 1) {  // the 256-wide tile is launched with K >= 256 only
-    wait_vm_barrier<0>();
-    stage(0, 0, false, true, false, fa0, fb0, fa1, fb1, sa0, sb0, sa1, sb1);
-    stage(1, 1, false, false, false, fa1, fb1, fa0, fb0, sa0, sb0, sa1, sb1);
+    kblock(0, 0, false, false, sa0, sb0, sa1, sb1);
     mfma_retire_pad();
     pin_acc();
-    epilogue(ring2, ring3);  // never loaded when K = 128
+    epilogue(kbuf1);  // never loaded when K = 128
   } else if (BM < 256) {
-    epilogue(ring0, ring1);  // K = 0: zeros
+    epilogue(kbuf0);  // K = 0: zeros
   }
 #endif
 }
@@ -578,16 +577,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
 template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW>
 void launch_tile(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
                  const uint8_t* b, int64_t ldb, const uint8_t* sb, void* c, int64_t ldc, int c_dtype,
-                 hipStream_t stream) {
-  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bs_kernel<BM, BN, STAGES, AFMT, BFMT, BKN, BROW>), dim3(tiles_m * tiles_n),
+                 int tiles_m, int tiles_n, int tile_first, int cells, int split, hipStream_t stream) {
+  if (cells <= 0) return;
+  hipLaunchKernelGGL((gemm_bs_kernel<BM, BN, STAGES, AFMT, BFMT, BKN, BROW>), dim3(cells << (2 * split)),
                      dim3(kThreads), 0, stream, (int)M, (int)N, (int)K, a, lda, sa, b, ldb, sb, c, ldc,
-                     c_dtype == 1 ? 1 : 0, tiles_m, tiles_n);
+                     c_dtype == 1 ? 1 : 0, tiles_m, tiles_n, tile_first, split);
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 // Tile choice: 256x256 (128x128 per wave, the lowest LDS traffic per MFMA) when
-// there are enough tiles to cover the 256 CUs, else 128x128.  Building with
-// -DMXFP8_GEMM_TILE=128 or 256 pins one of them (for tuning).
+// there are enough tiles to cover the CUs, else 128x128; a short last round
+// of 256x256 tiles runs as 128x128 quadrants.  Building with
+// -DMXFP8_GEMM_TILE=128 or 256 pins one tile size everywhere (for tuning).
 #ifndef MXFP8_GEMM_TILE
 #define MXFP8_GEMM_TILE 0
 #endif
@@ -595,14 +608,27 @@ template <int AFMT, int BFMT, bool BKN, bool BROW>
 void launch_shape(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
                   const uint8_t* b, int64_t ldb, const uint8_t* sb, void* c, int64_t ldc, int c_dtype,
                   hipStream_t stream) {
-  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int bm = (int)((M + 255) / 256), bn = (int)((N + 255) / 256), big_tiles = bm * bn;
+  const int cus = device_cus();
   // The 256-wide tile needs K >= 256: a separate single-K-block drain would
   // make the accumulators spill (merging three exit paths of 256 of them).
-  const bool big = K >= 256 && (MXFP8_GEMM_TILE == 256 || (MXFP8_GEMM_TILE == 0 && big_tiles >= 256));
-  if (big)
-    launch_tile<256, 256, 4, AFMT, BFMT, BKN, BROW>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
-  else
-    launch_tile<128, 128, 4, AFMT, BFMT, BKN, BROW>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+  const bool big = K >= 256 && (MXFP8_GEMM_TILE == 256 || (MXFP8_GEMM_TILE == 0 && big_tiles >= cus));
+  if (!big) {
+    const int sm = (int)((M + 127) / 128), sn = (int)((N + 127) / 128);
+    launch_tile<128, 128, 4, AFMT, BFMT, BKN, BROW>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, sm, sn, 0,
+                                                    sm * sn, 0, stream);
+    return;
+  }
+  // Last partial round: when its 256x256 tiles, cut in four, fit on the CUs
+  // in one round of 128x128 tiles, that round takes about a quarter as long.
+  const int tail = big_tiles % cus;
+  const bool split_tail = MXFP8_GEMM_TILE == 0 && big_tiles > cus && tail > 0 && 4 * tail <= cus;
+  const int main_cells = split_tail ? big_tiles - tail : big_tiles;
+  launch_tile<256, 256, 4, AFMT, BFMT, BKN, BROW>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, bm, bn, 0,
+                                                  main_cells, 0, stream);
+  if (split_tail)
+    launch_tile<128, 128, 4, AFMT, BFMT, BKN, BROW>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, bm, bn,
+                                                    main_cells, tail, 1, stream);
 }
 
 template <int AFMT, int BFMT>
