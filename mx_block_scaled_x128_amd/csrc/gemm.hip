@@ -143,20 +143,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int MT = WM / 32, NT = WN / 32;          // 32x32 MFMA tiles per wave
   // LDS: two K-block buffers, each holding both 64-wide stages of one
-  // 128-wide K block: the A tile [BM][128 B], the B tile ([BN][128 B], or
-  // [128 k][BN B] when B is [K][N]), then one dword per row of A and per
-  // column of B holding that K block's scale byte.  Whole 128-byte rows per
-  // load instruction: HBM/L2 lines are 128 bytes, and loading a row's two
-  // 64-byte halves in different stages fetched every line twice.
+  // 128-wide K block: the A tile [BM][128 B] and the B tile ([BN][128 B], or
+  // [128 k][BN B] when B is [K][N]).  Whole 128-byte rows per load
+  // instruction: HBM/L2 lines are 128 bytes, and loading a row's two 64-byte
+  // halves in different stages fetched every line twice.  (A buffer also
+  // hosts the epilogue's staging, hence its size.)
   constexpr int KBB = 128;                           // K bytes per buffer row
   constexpr int A_ST = BM * KBB, B_ST = BN * KBB;
-  constexpr int SA_OFF = A_ST + B_ST, SB_OFF = SA_OFF + kThreads * 4, PB = SB_OFF + kThreads * 4;
+  constexpr int STG = 4 * 32 * (BN / 2 * 4 + 16);    // epilogue staging (fp32 strips)
+  constexpr int PB = A_ST + B_ST > STG ? A_ST + B_ST : STG;
   constexpr int A_LOADS = A_ST / (kThreads * 16), B_LOADS = B_ST / (kThreads * 16);  // per K block, per thread
-  constexpr int SLOADS = 2;                          // scale loads per K block, per thread
   constexpr int CPR = BN / 16;
   static_assert(BM % 64 == 0 && BN % 64 == 0 && A_LOADS >= 1 && B_LOADS >= 1, "tile");
-  static_assert(BM <= kThreads && BN <= kThreads, "one scale slot per thread");
-  static_assert(A_LOADS + B_LOADS + SLOADS <= 63, "vmcnt range");
+  static_assert(BM <= kThreads && BN <= kThreads, "one scale entity per lane quarter");
+  static_assert(A_LOADS + B_LOADS + 8 <= 63, "vmcnt range");
+  // Scale groups: the scale bytes of 4 consecutive K blocks for each of 256
+  // tile rows (A) and columns (B), double-buffered.  Byte d = 4 e + s of a
+  // group area (one dword per byte: the LDS layout of 1-byte LDS-bound
+  // loads) holds entity e's scale for K block 4g + s.  Loading 4 K blocks
+  // at a time touches each row's scale line once per 4 K blocks instead of
+  // once per K block (rows are nkb bytes apart in [rows][K/128] scales).
+  constexpr int SG_OP = kThreads * 4 * 4;            // one operand's group area (bytes)
+  constexpr int SG = 2 * SG_OP;                      // A then B
   (void)STAGES;
 
   // One array per buffer; every access names its buffer with a compile-time
@@ -165,6 +173,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // into one buffer before reading the other.
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[PB];
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[PB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sgrp[2 * SG];
   auto buf_ptr = [&](int p) __attribute__((always_inline)) -> uint8_t* { return p == 0 ? kbuf0 : kbuf1; };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -227,51 +236,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   }
   const int64_t b_step = BKN ? (int64_t)KBB * ldb : KBB;
 
-  // Scale sources: thread t fetches the scale byte of tile row t (A) and of
-  // tile column t (B) for a K block; the byte lands zero-extended in dword t
-  // of the buffer's scale area (the LDS layout of 1-byte LDS-bound loads).
-  const uint8_t* sa_base = SA + (int64_t)m0 * nkb;
-  const uint32_t sa_off = (uint32_t)((min(m0 + tid, M - 1) - m0) * nkb);
-  const uint8_t* sb_base;
-  uint32_t sb_off;
-  int sb_step;
-  if (BROW) {
-    sb_base = SB + (int64_t)n0 * nkb;
-    sb_off = (uint32_t)((min(n0 + tid, N - 1) - n0) * nkb);
-    sb_step = 1;
-  } else {
-    const int nb = min((n0 + tid) >> 7, nnb - 1);
-    sb_base = SB;
-    sb_off = (uint32_t)(BKN ? nb : nb * nkb);
-    sb_step = BKN ? nnb : 1;
-  }
+  // Scale sources.  Group g's load instruction j of a wave (4 per operand)
+  // covers entities e = 16 (4 wave + j) + (lane >> 2), K block 4g + (lane & 3)
+  // (clamped to the last one; rows past M / N are clamped too).
+  const uint8_t* sa_base = uniform_opaque(SA + (int64_t)m0 * nkb);
+  const uint8_t* sb_base = uniform_opaque(BROW ? SB + (int64_t)n0 * nkb : SB);
+  auto sdma_group = [&](int grp) __attribute__((always_inline)) {
+    uint8_t* area = sgrp + (grp & 1) * SG;
+    const int kbs = min(4 * grp + (lane & 3), nkb - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = (wave * 4 + j) * 16 + (lane >> 2);
+      const uint32_t off = (uint32_t)(min(e, M - 1 - m0) * nkb + kbs);
+      __builtin_amdgcn_global_load_lds(sa_base + off, area + (wave * 4 + j) * 256, 1, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = (wave * 4 + j) * 16 + (lane >> 2);
+      uint32_t off;
+      if (BROW) {
+        off = (uint32_t)(min(e, N - 1 - n0) * nkb + kbs);
+      } else {
+        const int nb = min((n0 + e) >> 7, nnb - 1);
+        off = (uint32_t)(BKN ? kbs * nnb + nb : nb * nkb + kbs);
+      }
+      __builtin_amdgcn_global_load_lds(sb_base + off, area + SG_OP + (wave * 4 + j) * 256, 1, 0, 0);
+    }
+  };
 
   // LDS-bound loads of K block kb into buffer p, one instruction per item:
-  // items 0..SLOADS-1 are the scale bytes, then A_LOADS loads of A and
-  // B_LOADS of B.
-  constexpr int DMA_ITEMS = SLOADS + A_LOADS + B_LOADS;
+  // A_LOADS loads of A, then B_LOADS of B.
+  constexpr int DMA_ITEMS = A_LOADS + B_LOADS;
   struct Src {
-    const uint8_t *a, *b, *sa, *sb;
+    const uint8_t *a, *b;
   };
   auto dma_src = [&](int kb) __attribute__((always_inline)) {
     Src src;
     src.a = uniform_opaque(a_base + (int64_t)kb * KBB);
     src.b = uniform_opaque(b_base + (int64_t)kb * b_step);
-    src.sa = uniform_opaque(sa_base + kb);
-    src.sb = uniform_opaque(sb_base + (int64_t)kb * sb_step);
     return src;
   };
   auto dma_item = [&](int p, const Src& src, int item) __attribute__((always_inline)) {
     uint8_t* buf = buf_ptr(p);
-    if (item == 0) {
-      __builtin_amdgcn_global_load_lds(src.sa + sa_off, buf + SA_OFF + wave * 256, 1, 0, 0);
-    } else if (item == 1) {
-      __builtin_amdgcn_global_load_lds(src.sb + sb_off, buf + SB_OFF + wave * 256, 1, 0, 0);
-    } else if (item < SLOADS + A_LOADS) {
-      const int j = item - SLOADS;
-      __builtin_amdgcn_global_load_lds(src.a + a_off[j], buf + (j * 4 + wave) * 1024, 16, 0, 0);
+    if (item < A_LOADS) {
+      __builtin_amdgcn_global_load_lds(src.a + a_off[item], buf + (item * 4 + wave) * 1024, 16, 0, 0);
     } else {
-      const int j = item - SLOADS - A_LOADS;
+      const int j = item - A_LOADS;
       __builtin_amdgcn_global_load_lds(src.b + b_off[j], buf + A_ST + (j * 4 + wave) * 1024, 16, 0, 0);
     }
   };
@@ -281,15 +291,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
     for (int item = 0; item < DMA_ITEMS; ++item) dma_item(p, src, item);
   };
 
-  // Scale operands of the K block in buffer p.
-  const uint32_t sa_rd = opaque(SA_OFF + (wm * WM + (lane & 31)) * 4);
-  const uint32_t sb_rd = opaque(SB_OFF + (wn * WN + (lane & 31)) * 4);
-  auto read_scales = [&](int p, int (&sa)[MT], int (&sb)[NT]) __attribute__((always_inline)) {
-    const uint8_t* buf = buf_ptr(p);
+  // Scale operands of K block kb (from its group's area).
+  const uint32_t sa_rd = opaque((wm * WM + (lane & 31)) * 16);
+  const uint32_t sb_rd = opaque(SG_OP + (wn * WN + (lane & 31)) * 16);
+  auto read_scales = [&](int kb, int (&sa)[MT], int (&sb)[NT]) __attribute__((always_inline)) {
+    const uint8_t* area = sgrp + ((kb >> 2) & 1) * SG + (kb & 3) * 4;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) sa[mt] = *reinterpret_cast<const int*>(buf + sa_rd + mt * 128);
+    for (int mt = 0; mt < MT; ++mt) sa[mt] = *reinterpret_cast<const int*>(area + sa_rd + mt * 512);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sb[nt] = *reinterpret_cast<const int*>(buf + sb_rd + nt * 128);
+    for (int nt = 0; nt < NT; ++nt) sb[nt] = *reinterpret_cast<const int*>(area + sb_rd + nt * 512);
   };
 
   v16f acc[MT][NT];
@@ -380,18 +390,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // The stage multiplies fragments (ca, cb) with scales (csa, csb).
   // dma_p >= 0: load K block dma_kb into buffer dma_p meanwhile.
   // rd_p >= 0: read the fragments of stage half rd_h of buffer rd_p into
-  // (na, nb); with do_sc also that buffer's scales into (nsa, nsb).
-  auto stage = [&](int dma_p, int dma_kb, int rd_p, int rd_h, bool do_sc, const v8i (&ca)[MT],
+  // (na, nb); with do_sc also K block sc_kb's scales into (nsa, nsb).
+  // grp >= 0: load scale group grp.
+  auto stage = [&](int dma_p, int dma_kb, int rd_p, int rd_h, bool do_sc, int sc_kb, int grp, const v8i (&ca)[MT],
                    const v8i (&cb)[NT], v8i (&na)[MT], v8i (&nb)[NT], const int (&csa)[MT],
                    const int (&csb)[NT], int (&nsa)[MT], int (&nsb)[NT]) __attribute__((always_inline)) {
-    Src src = {nullptr, nullptr, nullptr, nullptr};
+    Src src = {nullptr, nullptr};
     if (dma_p >= 0) src = dma_src(dma_kb);
 #pragma unroll
     for (int i = 0; i < MFMAS; ++i) {
       const int mt = i / NT, nt = i % NT;
       acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[nt], ca[mt], acc[mt][nt], BFMT, AFMT, 0,
                                                                    csb[nt], 0, csa[mt]);
-      if (rd_p >= 0 && do_sc && i == 0) read_scales(rd_p, nsa, nsb);
+      if (rd_p >= 0 && do_sc && i == 0) read_scales(sc_kb, nsa, nsb);
+      if (grp >= 0 && i == 0) sdma_group(grp);  // after the scale read: same array
 #pragma unroll
       for (int item = 0; item < DS_ITEMS; ++item)
         if (rd_p >= 0 && item * DS_SPAN / DS_ITEMS == i) ds_item(rd_p, rd_h, item, na, nb);
@@ -416,16 +428,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // fragments and scales.  One barrier per K block.
   // kblock(p, kb, ...): K block kb in buffer p with scale set (csa, csb);
   // dma: load K block kb+2; next: kb+1 exists (read its scales into (nsa, nsb)).
-  auto kblock = [&](int p, int kb, bool dma, bool next, const int (&csa)[MT], const int (&csb)[NT],
+  // sg: also load scale group (kb >> 2) + 1 (kb even, in the main loop's
+  // first K block of each pair).  At kb = 0 mod 4 that group first lands in
+  // its area, whose previous group was last read one K block earlier; at
+  // kb = 2 mod 4 the same bytes are written again (harmless, and no branch
+  // in the instruction stream); a group past the last K block loads clamped
+  // bytes nobody reads.  A group is read from 2 to 3 K blocks later on.
+  auto kblock = [&](int p, int kb, bool dma, bool next, bool sg, const int (&csa)[MT], const int (&csb)[NT],
                     int (&nsa)[MT], int (&nsb)[NT]) __attribute__((always_inline)) {
-    stage(-1, 0, p, 1, false, fa0, fb0, fa1, fb1, csa, csb, nsa, nsb);
+    stage(-1, 0, p, 1, false, 0, -1, fa0, fb0, fa1, fb1, csa, csb, nsa, nsb);
     if (dma || next) wait_vm_barrier<0>();
-    stage(dma ? p : -1, kb + 2, next ? (p ^ 1) : -1, 0, next, fa1, fb1, fa0, fb0, csa, csb, nsa, nsb);
+    stage(dma ? p : -1, kb + 2, next ? (p ^ 1) : -1, 0, next, kb + 1, sg ? (kb >> 2) + 1 : -1, fa1, fb1, fa0,
+          fb0, csa, csb, nsa, nsb);
   };
 
   // ---- prologue: K blocks 0 and 1 in flight, then K block 0's first
   // fragments and scales.  K block kb sits in buffer kb % 2.
   if (nkb > 0) {
+    sdma_group(0);
     dma_kblock(0, 0);
     if (nkb > 1) {
       dma_kblock(1, 1);
@@ -446,11 +466,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   int kb = 0;
 #pragma nounroll
   for (; kb + 1 < main_kb; kb += 2) {  // two K blocks: buffers 0, 1; scale sets 0, 1
-    kblock(0, kb, true, true, sa0, sb0, sa1, sb1);
-    kblock(1, kb + 1, true, true, sa1, sb1, sa0, sb0);
+    kblock(0, kb, true, true, true, sa0, sb0, sa1, sb1);
+    kblock(1, kb + 1, true, true, false, sa1, sb1, sa0, sb0);
   }
   if (kb < main_kb) {
-    kblock(0, kb, true, true, sa0, sb0, sa1, sb1);
+    kblock(0, kb, true, true, false, sa0, sb0, sa1, sb1);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) sa0[mt] = sa1[mt];
 #pragma unroll
@@ -558,13 +578,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // its own epilogue, in a buffer nobody reads after the drain's barrier.
   if (nkb >= 2) {
     const int p = nkb & 1;  // buffer of K block nkb - 2
-    kblock(p, nkb - 2, false, true, sa0, sb0, sa1, sb1);
-    kblock(p ^ 1, nkb - 1, false, false, sa1, sb1, sa0, sb0);
+    kblock(p, nkb - 2, false, true, false, sa0, sb0, sa1, sb1);
+    kblock(p ^ 1, nkb - 1, false, false, false, sa1, sb1, sa0, sb0);
     mfma_retire_pad();
     pin_acc();
     epilogue(buf_ptr(p));
   } else if (BM < 256 && nkb == 1) {  // the 256-wide tile is launched with K >= 256 only
-    kblock(0, 0, false, false, sa0, sb0, sa1, sb1);
+    kblock(0, 0, false, false, false, sa0, sb0, sa1, sb1);
     mfma_retire_pad();
     pin_acc();
     epilogue(kbuf1);  // never loaded when K = 128
