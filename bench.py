@@ -7,8 +7,11 @@ round-up scales) on seeded synthetic bf16 tensors already resident in HBM:
   2. fp8_quantize_block  W [8960 x 1536] bf16 -> codes + scales
   3. fp8_block_scaled_gemm  Y = Xq * Wq^T, M=4096 N=8960 K=1536, fp32 accumulate, bf16 out
 `value` is the whole step's throughput in TFLOP/s (2*M*N*K per step / step
-time).  Each kernel is also timed with events on the stream it runs on, and
-the dominant kernel (the GEMM) is reported against the dense FP8 MFMA peak.
+time), with the step's launches captured once in a HIP graph and replayed
+(the launches are asynchronous and allocate nothing, so a replay is the same
+work without the host's per-launch cost).  In a separate eager pass each
+entry point is timed with events on the stream it runs on, and the dominant
+one (the GEMM) is reported against the dense FP8 MFMA peak.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 
 Other workloads (--workload): dgrad7b, wgrad, mxstress -- for the per-kernel
@@ -74,6 +77,39 @@ class KernelTimer:
         return float(np.mean(self.times[name]))
 
 
+class _NoTimer:
+    def run(self, name, fn):
+        return fn()
+
+
+def time_graph(step, steps, warmup, outputs):
+    """Captures one step in a HIP graph, checks that a replay reproduces the eager step's
+    outputs bit for bit, then times `steps` replays (after `warmup`) between device
+    synchronisations.  Returns seconds per step."""
+    import torch
+    step(_NoTimer())
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outputs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(_NoTimer())
+    for o in outputs:
+        o.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    for o, r in zip(outputs, ref):
+        if not torch.equal(o, r):
+            raise RuntimeError("graph replay differs from the eager step")
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
 def time_steps(step, steps, warmup):
     import torch
     timer = KernelTimer()
@@ -107,7 +143,7 @@ def _check(st, what):
 
 def fprop_step_fn(t):
     """The step through the C-ABI entry points with outputs allocated once, so the events
-    bracket exactly one kernel launch each."""
+    bracket exactly one entry point each.  Returns (step, outputs)."""
     import torch
     import mx_block_scaled_x128_amd as mx
     x, w = t["x"], t["w"]
@@ -119,9 +155,9 @@ def fprop_step_fn(t):
     wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
     ws = torch.empty((N // 128, K // 128), dtype=torch.uint8, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream().cuda_stream
 
     def step(timer):
+        stream = torch.cuda.current_stream().cuda_stream
         _check(timer.run("quant_token_x", lambda: mx.fp8_quantize_token(
             x.data_ptr(), mx.BF16, M, K, K, mx.ROW, mx.E4M3, xq.data_ptr(), K, xs.data_ptr(), stream)),
             "fp8_quantize_token")
@@ -131,7 +167,7 @@ def fprop_step_fn(t):
         _check(timer.run("gemm", lambda: mx.fp8_block_scaled_gemm(
             M, N, K, xq.data_ptr(), K, mx.E4M3, xs.data_ptr(), wq.data_ptr(), K, mx.E4M3, mx.B_NK,
             ws.data_ptr(), mx.SCALE_BLOCK128, y.data_ptr(), N, mx.BF16, stream)), "fp8_block_scaled_gemm")
-    return step
+    return step, [xq, xs, wq, ws, y]
 
 
 def cpu_baseline_fprop(host, rows):
@@ -176,8 +212,9 @@ def bench_fprop(args):
     t = fprop_setup()
     M, K = t["x"].shape
     N = t["w"].shape[0]
-    step = fprop_step_fn(t)
-    per_step, timer = time_steps(step, args.steps, args.warmup)
+    step, outputs = fprop_step_fn(t)
+    per_step_eager, timer = time_steps(step, args.steps, args.warmup)
+    per_step = time_graph(step, args.steps, args.warmup, outputs)
     flops = 2.0 * M * N * K
     g = timer.mean("gemm")
     qx = timer.mean("quant_token_x")
@@ -188,6 +225,7 @@ def bench_fprop(args):
     line = {
         "metric": METRIC, "value": round(flops / per_step / 1e12, 3), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(per_step * 1e3, 4),
+        "ms_per_step_eager": round(per_step_eager * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
         "data": "synthetic (seeded numpy PCG64; bf16 inputs resident in HBM before timing)",
         "config": {"workload": "fprop1p5b: token-quantize X 4096x1536 bf16 (1x128, E4M3) + block-quantize "
@@ -230,8 +268,10 @@ def bench_other(args):
     import torch
     import mx_block_scaled_x128_amd as mx
     import synth
-    stream = torch.cuda.current_stream().cuda_stream
     u8 = dict(dtype=torch.uint8, device="cuda")
+
+    def cur():
+        return torch.cuda.current_stream().cuda_stream
     kern = {}
     if args.workload == "dgrad7b":
         d = synth.dgrad7b()
@@ -244,6 +284,7 @@ def bench_other(args):
         y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
 
         def step(timer):
+            stream = cur()
             _check(timer.run("quant_token_dy", lambda: mx.fp8_quantize_token(
                 dy.data_ptr(), mx.BF16, M, K, K, mx.ROW, mx.E5M2, gq.data_ptr(), K, gs.data_ptr(), stream)), "q")
             _check(timer.run("quant_block_w", lambda: mx.fp8_quantize_block(
@@ -252,6 +293,7 @@ def bench_other(args):
                 M, N, K, gq.data_ptr(), K, mx.E5M2, gs.data_ptr(), wq.data_ptr(), N, mx.E4M3, mx.B_KN,
                 ws.data_ptr(), mx.SCALE_BLOCK128, y.data_ptr(), N, mx.BF16, stream)), "gemm")
         sizes = {"quant_token_dy": bytes_token(M, K, 2), "quant_block_w": bytes_block(K, N, 2)}
+        outputs = [gq, gs, wq, ws, y]
         flops = 2.0 * M * N * K
         desc = "dgrad7b: token-quantize dY 8192x18944 bf16 (E5M2) + block-quantize W 18944x3584 (E4M3) + GEMM " \
                "M=8192 N=3584 K=18944 (B stored [K][N]) bf16 out"
@@ -265,6 +307,7 @@ def bench_other(args):
         y = torch.empty((C, C), dtype=torch.float32, device="cuda")
 
         def step(timer):
+            stream = cur()
             _check(timer.run("quant_col_x", lambda: mx.fp8_quantize_token(
                 x.data_ptr(), mx.BF16, T, C, C, mx.COL_T, mx.E4M3, xq.data_ptr(), T, xs.data_ptr(), stream)), "q")
             _check(timer.run("quant_col_dy", lambda: mx.fp8_quantize_token(
@@ -273,6 +316,7 @@ def bench_other(args):
                 C, C, T, gq.data_ptr(), T, mx.E5M2, gs.data_ptr(), xq.data_ptr(), T, mx.E4M3, mx.B_NK,
                 xs.data_ptr(), mx.SCALE_ROW128, y.data_ptr(), C, mx.F32, stream)), "gemm")
         sizes = {"quant_col_x": bytes_token(T, C, 2), "quant_col_dy": bytes_token(T, C, 2)}
+        outputs = [xq, xs, gq, gs, y]
         M = N = C
         K = T
         flops = 2.0 * M * N * K
@@ -284,15 +328,18 @@ def bench_other(args):
         q, sc, cn = torch.empty((R, C), **u8), torch.empty((R, C // 32), **u8), torch.empty((R, C // 32), **u8)
 
         def step(timer):
+            stream = cur()
             for j in range(64):
                 _check(timer.run("mx_quant", lambda: mx.mx_quantize(
                     xs_[j].data_ptr(), mx.F32, R, C, C, mx.E4M3, mx.RULE_FLOOR, q.data_ptr(), C, sc.data_ptr(),
                     cn.data_ptr(), stream)), "mx")
         sizes = {"mx_quant": R * C * 5 + 2 * R * (C // 32)}
+        outputs = [q, sc, cn]
         flops = 0.0
         M = N = K = 0
         desc = "mxstress: 64 tensors 4096x4096 fp32, MX 32-element E4M3 blocks, OCP floor scales, clamp counts"
-    per_step, timer = time_steps(step, args.steps, args.warmup)
+    per_step_eager, timer = time_steps(step, args.steps, args.warmup)
+    per_step = time_graph(step, args.steps, args.warmup, outputs)
     for name, b in sizes.items():
         t = timer.mean(name)
         kern[name] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
@@ -311,7 +358,8 @@ def bench_other(args):
                 "frac": kern["mx_quant"]["frac_hbm_peak"], "traffic": None}
     return {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(per_step * 1e3, 4), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(per_step * 1e3, 4),
+        "ms_per_step_eager": round(per_step_eager * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8", "data": "synthetic (seeded numpy PCG64)",
         "config": {"workload": desc, "M": M, "N": N, "K": K}, "kernels": kern, "roofline": roof,
         "cpu_baseline": None,
