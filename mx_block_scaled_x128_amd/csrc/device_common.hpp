@@ -122,14 +122,35 @@ __device__ __forceinline__ uint32_t sum_quad(uint32_t v) {
 __device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f) & 0x7FFFFFFFu; }
 
 // Loads of 8 consecutive input elements as fp32 (16 B for bf16, 32 B for fp32).
+typedef unsigned int nt_u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming stores (non-temporal): output bytes are written once (measured:
+// 10-25 % faster tile quantizers).
+__device__ __forceinline__ void store_nt(uint8_t* p, uint2 v) {
+  __builtin_nontemporal_store(nt_u32x2{v.x, v.y}, reinterpret_cast<nt_u32x2*>(p));
+}
+__device__ __forceinline__ void store_nt(uint8_t* p, uint4 v) {
+  __builtin_nontemporal_store(nt_u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_u32x4*>(p));
+}
+
+// Eight input elements as fp32.  NT: a non-temporal load (measured: it helps
+// the row quantizer, whose lanes stream along rows, and hurts the tile
+// quantizers, whose waves hop between rows).
+template <bool NT>
 __device__ __forceinline__ void load8(const uint16_t* p, float (&f)[8]) {
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const nt_u32x4 v = NT ? __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p))
+                        : *reinterpret_cast<const nt_u32x4*>(p);
   f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
   f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
+template <bool NT>
 __device__ __forceinline__ void load8(const float* p, float (&f)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  const nt_f32x4 a = NT ? __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p))
+                        : *reinterpret_cast<const nt_f32x4*>(p);
+  const nt_f32x4 b = NT ? __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p + 4))
+                        : *reinterpret_cast<const nt_f32x4*>(p + 4);
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }

@@ -9,7 +9,8 @@
 //
 // Every kernel reads its input once (16-byte vector loads, 8 elements per
 // lane), reduces amax with DPP inside the wavefront (LDS only where a group
-// spans waves), and writes packed codes (8 bytes per lane).
+// spans waves), and writes packed codes (8 bytes per lane) with non-temporal
+// stores.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(
       grp[u] = g;
       gvalid[u] = item < total_items && g < ngroups;
       act[u] = gvalid[u] && c < cols;
-      if (act[u]) load8(x + (int64_t)r * ldx + c, f[u]);
+      if (act[u]) load8<true>(x + (int64_t)r * ldx + c, f[u]);
       else zero8(f[u]);
     }
 #pragma unroll
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(
       const int e = scale_exp_ceil<FMT>(m);
       const float sc = pow2_neg(e);
       if (act[u])
-        *reinterpret_cast<uint2*>(q + (int64_t)row[u] * ldq + grp[u] * 128 + sub * 8) = codes8<FMT>(f[u], sc);
+        store_nt(q + (int64_t)row[u] * ldq + grp[u] * 128 + sub * 8, codes8<FMT>(f[u], sc));
       if (sub == 0 && gvalid[u]) s[(int64_t)row[u] * ngroups + grp[u]] = (uint8_t)(e + 127);
     }
   }
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void quant_col_t_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t r = t0 + tr * 8 + i;
-    if (cact && r < rows) load8(x + (int64_t)r * ldx + c0 + tc * 8, f[i]);
+    if (cact && r < rows) load8<false>(x + (int64_t)r * ldx + c0 + tc * 8, f[i]);
     else zero8(f[i]);
   }
   uint32_t m[8];
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void quant_col_t_kernel(
     if (c0 + ch < cols && t0 + ck * 16 < rows) {
       const uint2 a = *reinterpret_cast<const uint2*>(tile + ch * kColPitch + ck * 16);
       const uint2 b = *reinterpret_cast<const uint2*>(tile + ch * kColPitch + ck * 16 + 8);
-      *reinterpret_cast<uint4*>(qt + (int64_t)(c0 + ch) * ldq + t0 + ck * 16) = make_uint4(a.x, a.y, b.x, b.y);
+      store_nt(qt + (int64_t)(c0 + ch) * ldq + t0 + ck * 16, make_uint4(a.x, a.y, b.x, b.y));
     }
   }
 }
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t r = r0 + tr * 8 + i;
-    if (cact && r < rows) load8(w + (int64_t)r * ldw + c0 + tc * 8, f[i]);
+    if (cact && r < rows) load8<false>(w + (int64_t)r * ldw + c0 + tc * 8, f[i]);
     else zero8(f[i]);
   }
   uint32_t m = 0;
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(
   for (int i = 0; i < 8; ++i) {
     const uint32_t r = r0 + tr * 8 + i;
     if (cact && r < rows)
-      *reinterpret_cast<uint2*>(q + (int64_t)r * ldq + c0 + tc * 8) = codes8<FMT>(f[i], sc);
+      store_nt(q + (int64_t)r * ldq + c0 + tc * 8, codes8<FMT>(f[i], sc));
   }
   if (tid == 0) s[(int64_t)blockIdx.y * nbc + blockIdx.x] = (uint8_t)(e + 127);
 }
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(
       row[u] = r;
       blk[u] = b;
       act[u] = item < total_items && b < nblk;
-      if (act[u]) load8(x + (int64_t)r * ldx + b * 32 + sub * 8, f[u]);
+      if (act[u]) load8<false>(x + (int64_t)r * ldx + b * 32 + sub * 8, f[u]);
       else zero8(f[u]);
     }
 #pragma unroll
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(
         uint2 o;
         o.x = cvt4<FMT>(v[0], v[1], v[2], v[3]);
         o.y = cvt4<FMT>(v[4], v[5], v[6], v[7]);
-        *reinterpret_cast<uint2*>(q + (int64_t)row[u] * ldq + blk[u] * 32 + sub * 8) = o;
+        store_nt(q + (int64_t)row[u] * ldq + blk[u] * 32 + sub * 8, o);
         if (sub == 0) {
           s[(int64_t)row[u] * nblk + blk[u]] = (uint8_t)(e + 127);
           if (COUNTS) cnt[(int64_t)row[u] * nblk + blk[u]] = (uint8_t)n;
