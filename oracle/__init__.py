@@ -70,6 +70,10 @@ def _load():
         lib.orc_gemm_elems.argtypes = [I64, I64, I64, P, I64, I, P, P, I64, I, I, P, I,
                                        P, P, I64, P, P]
         lib.orc_gemm_elems.restype = None
+        lib.orc_mx_gemm.argtypes = [I64, I64, I64, P, I64, I, P, P, I64, I, P, I64, I64, P, P, I64]
+        lib.orc_mx_gemm.restype = None
+        lib.orc_mx_gemm_elems.argtypes = [I64, I64, I64, P, I64, I, P, P, I64, I, P, P, P, I64, P, P]
+        lib.orc_mx_gemm_elems.restype = None
         lib.orc_decode_array.argtypes = [I, P, I64, P]
         lib.orc_encode_array.argtypes = [I, P, I64, P]
         lib.orc_encode_f32_range.argtypes = [I, ctypes.c_uint32, I64, P]
@@ -268,6 +272,55 @@ def gemm_elems(a, sa, a_fmt, b, sb, b_fmt, ii, jj, b_layout=B_NK, b_scale=B_SCAL
     def job(i0, i1):
         return lambda: lib.orc_gemm_elems(
             M, N, K, _ptr(a), K, a_fmt, _ptr(sa), _ptr(b), ldb, b_fmt, b_layout, _ptr(sb), b_scale,
+            ctypes.c_void_p(ii.ctypes.data + 8 * i0), ctypes.c_void_p(jj.ctypes.data + 8 * i0), i1 - i0,
+            ctypes.c_void_p(y.ctypes.data + 8 * i0), ctypes.c_void_p(t.ctypes.data + 8 * i0))
+    _run([job(i0, i1) for i0, i1 in _split(n, threads)])
+    return y, t
+
+
+def _mx_operands(a, sa, b, sb):
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    sb = np.ascontiguousarray(sb, dtype=np.uint8)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("A and B disagree on K")
+    nkc = -(-K // 32)
+    if sa.shape != (M, nkc) or sb.shape != (N, nkc):
+        raise ValueError("MX scales must be [rows][K/32]")
+    return a, sa, b, sb, M, N, K
+
+
+def mx_gemm(a, sa, a_fmt, b, sb, b_fmt, threads=1):
+    """MX GEMM: A [M][K] with scales [M][K/32], B stored [N][K] with scales
+    [N][K/32]; y = sum_k a(m,k) b(n,k), t = sum_k |a b|, fp64 [M][N]."""
+    lib = _load()
+    a, sa, b, sb, M, N, K = _mx_operands(a, sa, b, sb)
+    y = np.empty((M, N), np.float64)
+    t = np.empty((M, N), np.float64)
+
+    def job(m0, m1):
+        return lambda: lib.orc_mx_gemm(M, N, K, _ptr(a), K, a_fmt, _ptr(sa), _ptr(b), K, b_fmt, _ptr(sb),
+                                       m0, m1, _ptr(y), _ptr(t), N)
+    _run([job(m0, m1) for m0, m1 in _split(M, threads)])
+    return y, t
+
+
+def mx_gemm_elems(a, sa, a_fmt, b, sb, b_fmt, ii, jj, threads=1):
+    """The MX sums for the listed output elements (ii[i], jj[i])."""
+    lib = _load()
+    a, sa, b, sb, M, N, K = _mx_operands(a, sa, b, sb)
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    n = ii.size
+    y = np.empty(n, np.float64)
+    t = np.empty(n, np.float64)
+
+    def job(i0, i1):
+        return lambda: lib.orc_mx_gemm_elems(
+            M, N, K, _ptr(a), K, a_fmt, _ptr(sa), _ptr(b), K, b_fmt, _ptr(sb),
             ctypes.c_void_p(ii.ctypes.data + 8 * i0), ctypes.c_void_p(jj.ctypes.data + 8 * i0), i1 - i0,
             ctypes.c_void_p(y.ctypes.data + 8 * i0), ctypes.c_void_p(t.ctypes.data + 8 * i0))
     _run([job(i0, i1) for i0, i1 in _split(n, threads)])

@@ -364,6 +364,65 @@ void orc_gemm_elems(int64_t M, int64_t N, int64_t K,
   }
 }
 
+/* MX GEMM ["Characterization and Mitigation of Training Instabilities in
+ * Microscaling Formats", "What carries the argument": a block of 32
+ * consecutive elements shares one E8M0 scale, the element's value being the
+ * scale times the decoded FP8 element; the GEMM runs on such operands].
+ * Both operands are blocked along K: A [M][K] with scales [M][K/32], B stored
+ * [N][K] with scales [N][K/32] (what the MX quantizer produces along rows).
+ * y and t as in orc_gemm, for rows [m0, m1). */
+static double mx_value(int64_t K, const uint8_t* x, int64_t ldx, int fmt, const uint8_t* s,
+                       int64_t r, int64_t k) {
+  const int64_t nkc = ceil_div(K, 32);
+  return ldexp(orc_decode(fmt, x[r * ldx + k]), (int)s[r * nkc + k / 32] - 127);
+}
+
+void orc_mx_gemm(int64_t M, int64_t N, int64_t K,
+                 const uint8_t* a, int64_t lda, int a_fmt, const uint8_t* sa,
+                 const uint8_t* b, int64_t ldb, int b_fmt, const uint8_t* sb,
+                 int64_t m0, int64_t m1, double* y, double* t, int64_t ldy) {
+  (void)M;
+  double* bd = (double*)malloc(sizeof(double) * (size_t)(N * K > 0 ? N * K : 1));
+  double* ad = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+  if (!bd || !ad) { free(bd); free(ad); abort(); }
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) bd[n * K + k] = mx_value(K, b, ldb, b_fmt, sb, n, k);
+  for (int64_t m = m0; m < m1; ++m) {
+    for (int64_t k = 0; k < K; ++k) ad[k] = mx_value(K, a, lda, a_fmt, sa, m, k);
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0, mag = 0.0;
+      const double* bn = bd + n * K;
+      for (int64_t k = 0; k < K; ++k) {
+        const double p = ad[k] * bn[k];
+        acc += p;
+        mag += fabs(p);
+      }
+      y[m * ldy + n] = acc;
+      t[m * ldy + n] = mag;
+    }
+  }
+  free(ad);
+  free(bd);
+}
+
+void orc_mx_gemm_elems(int64_t M, int64_t N, int64_t K,
+                       const uint8_t* a, int64_t lda, int a_fmt, const uint8_t* sa,
+                       const uint8_t* b, int64_t ldb, int b_fmt, const uint8_t* sb,
+                       const int64_t* ii, const int64_t* jj, int64_t n, double* y, double* t) {
+  (void)M;
+  (void)N;
+  for (int64_t i = 0; i < n; ++i) {
+    double acc = 0.0, mag = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double p = mx_value(K, a, lda, a_fmt, sa, ii[i], k) * mx_value(K, b, ldb, b_fmt, sb, jj[i], k);
+      acc += p;
+      mag += fabs(p);
+    }
+    y[i] = acc;
+    t[i] = mag;
+  }
+}
+
 /* ---------------------------------------------------------------------- */
 /* Array helpers for the tests (loops over the scalar functions above)      */
 /* ---------------------------------------------------------------------- */

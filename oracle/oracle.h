@@ -51,6 +51,15 @@ void orc_gemm_elems(int64_t M, int64_t N, int64_t K,
                     const uint8_t* sb, int b_scale,
                     const int64_t* ii, const int64_t* jj, int64_t n, double* y, double* t);
 
+void orc_mx_gemm(int64_t M, int64_t N, int64_t K,
+                 const uint8_t* a, int64_t lda, int a_fmt, const uint8_t* sa,
+                 const uint8_t* b, int64_t ldb, int b_fmt, const uint8_t* sb,
+                 int64_t m0, int64_t m1, double* y, double* t, int64_t ldy);
+void orc_mx_gemm_elems(int64_t M, int64_t N, int64_t K,
+                       const uint8_t* a, int64_t lda, int a_fmt, const uint8_t* sa,
+                       const uint8_t* b, int64_t ldb, int b_fmt, const uint8_t* sb,
+                       const int64_t* ii, const int64_t* jj, int64_t n, double* y, double* t);
+
 void orc_decode_array(int fmt, const uint8_t* codes, int64_t n, double* out);
 void orc_encode_array(int fmt, const double* x, int64_t n, uint8_t* out);
 void orc_encode_f32_range(int fmt, uint32_t start, int64_t n, uint8_t* out);

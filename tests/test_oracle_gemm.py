@@ -137,3 +137,76 @@ def test_matches_numpy_matmul_of_torch_decoded(b_layout, b_scale):
     jj = np.array([0, 385, 128, 200], np.int64)
     ye, te = oracle.gemm_elems(a, sa, 0, b_store, sb_store, 1, ii, jj, b_layout, b_scale)
     assert np.array_equal(ye, y[ii, jj]) and np.array_equal(te, t[ii, jj])
+
+
+# ---------------------------------------------------------------- MX GEMM
+# Pins for oracle.mx_gemm: operands scaled per 32-element block along K
+# ("Characterization and Mitigation of Training Instabilities in Microscaling
+# Formats", "What carries the argument").
+
+@pytest.mark.parametrize("a_fmt,b_fmt", [(0, 0), (1, 0), (0, 1)])
+@pytest.mark.parametrize("K", [32, 96, 256])
+def test_mx_tiny_exact_rational(a_fmt, b_fmt, K):
+    M, N = 3, 4
+    a = synth.random_codes(61 + K, (M, K), a_fmt)
+    b = synth.random_codes(62 + K, (N, K), b_fmt)
+    sa = synth.random_scale_bytes(63 + K, (M, K // 32), 100, 150)
+    sb = synth.random_scale_bytes(64 + K, (N, K // 32), 100, 150)
+    y, t = oracle.mx_gemm(a, sa, a_fmt, b, sb, b_fmt)
+    for i in range(M):
+        for j in range(N):
+            acc = Fraction(0)
+            mag = Fraction(0)
+            for k in range(K):
+                p = (exact_value(int(a[i, k]), a_fmt) * Fraction(2) ** (int(sa[i, k // 32]) - 127)
+                     * exact_value(int(b[j, k]), b_fmt) * Fraction(2) ** (int(sb[j, k // 32]) - 127))
+                acc += p
+                mag += abs(p)
+            bound = mag * (K - 1) * Fraction(2) ** -53
+            assert abs(Fraction(y[i, j]) - acc) <= bound
+            assert abs(Fraction(t[i, j]) - mag) <= bound
+
+
+def test_mx_scale_byte_bump_doubles_one_32_block():
+    M, N, K = 2, 3, 256
+    a = synth.random_codes(71, (M, K), 0)
+    b = synth.random_codes(72, (N, K), 0)
+    sa = synth.random_scale_bytes(73, (M, K // 32))
+    sb = synth.random_scale_bytes(74, (N, K // 32))
+    y0, _ = oracle.mx_gemm(a, sa, 0, b, sb, 0)
+    sb2 = sb.copy()
+    sb2[2, 5] += 1  # column 2, k in [160, 192)
+    y1, _ = oracle.mx_gemm(a, sa, 0, b, sb2, 0)
+    a_blk = np.zeros_like(a)
+    a_blk[:, 160:192] = a[:, 160:192]
+    yb, _ = oracle.mx_gemm(a_blk, sa, 0, b, sb, 0)
+    assert np.array_equal(y1[:, :2], y0[:, :2])
+    assert np.allclose(y1[:, 2] - y0[:, 2], yb[:, 2], rtol=2.0 ** -45, atol=0)
+
+
+def test_mx_matches_numpy_matmul_of_torch_decoded():
+    M, N, K = 24, 40, 320
+    a = synth.random_codes(81, (M, K), 1)
+    b = synth.random_codes(82, (N, K), 0)
+    sa = synth.random_scale_bytes(83, (M, K // 32))
+    sb = synth.random_scale_bytes(84, (N, K // 32))
+    A = torch_dec(a, 1) * 2.0 ** (np.repeat(sa, 32, axis=1).astype(np.float64) - 127)
+    B = torch_dec(b, 0) * 2.0 ** (np.repeat(sb, 32, axis=1).astype(np.float64) - 127)
+    y, t = oracle.mx_gemm(a, sa, 1, b, sb, 0, threads=4)
+    mag = np.abs(A) @ np.abs(B).T
+    assert np.allclose(y, A @ B.T, rtol=0, atol=K * 2.0 ** -52 * mag.max())
+    assert np.allclose(t, mag, rtol=K * 2.0 ** -52, atol=0)
+    yi, ti = oracle.mx_gemm_elems(a, sa, 1, b, sb, 0, np.array([0, 5, 23]), np.array([39, 0, 17]))
+    assert np.array_equal(yi, y[[0, 5, 23], [39, 0, 17]]) and np.array_equal(ti, t[[0, 5, 23], [39, 0, 17]])
+
+
+def test_mx_with_uniform_128_scales_equals_block_gemm():
+    """Four equal 32-block scales per 128 block give the per-(row, 128) GEMM."""
+    M, N, K = 6, 10, 384
+    a = synth.random_codes(91, (M, K), 0)
+    b = synth.random_codes(92, (N, K), 1)
+    sa128 = synth.random_scale_bytes(93, (M, K // 128))
+    sb128 = synth.random_scale_bytes(94, (N, K // 128))
+    y_mx, t_mx = oracle.mx_gemm(a, np.repeat(sa128, 4, axis=1), 0, b, np.repeat(sb128, 4, axis=1), 1)
+    y_bs, t_bs = oracle.gemm(a, sa128, 0, b, sb128, 1, oracle.B_NK, oracle.B_SCALE_ROW)
+    assert np.array_equal(y_mx, y_bs) and np.array_equal(t_mx, t_bs)
