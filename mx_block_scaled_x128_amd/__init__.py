@@ -8,9 +8,9 @@ entry point raises -- there is no fallback path.
 
 Low-level entry points carry the C names and signatures (pointers as ints):
   fp8_quantize_token, fp8_quantize_block, mx_quantize, fp8_block_scaled_gemm,
-  mxfp8_status_string, mxfp8_version.
+  mx_gemm, mxfp8_status_string, mxfp8_version.
 Tensor conveniences allocate outputs with torch and call them:
-  quantize_token, quantize_block, quantize_mx, block_scaled_gemm.
+  quantize_token, quantize_block, quantize_mx, block_scaled_gemm, mx_scaled_gemm.
 """
 import ctypes
 import os
@@ -19,9 +19,9 @@ import threading
 __all__ = [
     "E4M3", "E5M2", "F32", "BF16", "ROW", "COL_T", "RULE_CEIL", "RULE_FLOOR", "B_NK", "B_KN",
     "SCALE_BLOCK128", "SCALE_ROW128", "MxFp8Error", "library_path", "load_library",
-    "fp8_quantize_token", "fp8_quantize_block", "mx_quantize", "fp8_block_scaled_gemm",
+    "fp8_quantize_token", "fp8_quantize_block", "mx_quantize", "fp8_block_scaled_gemm", "mx_gemm",
     "mxfp8_status_string", "mxfp8_version",
-    "quantize_token", "quantize_block", "quantize_mx", "block_scaled_gemm",
+    "quantize_token", "quantize_block", "quantize_mx", "block_scaled_gemm", "mx_scaled_gemm",
 ]
 
 # enum values of include/mxfp8.h
@@ -67,6 +67,8 @@ def load_library():
         lib.mx_quantize.restype = I
         lib.fp8_block_scaled_gemm.argtypes = [I64, I64, I64, P, I64, I, P, P, I64, I, I, P, I, P, I64, I, P]
         lib.fp8_block_scaled_gemm.restype = I
+        lib.mx_gemm.argtypes = [I64, I64, I64, P, I64, I, P, P, I64, I, P, P, I64, I, P]
+        lib.mx_gemm.restype = I
         lib.mxfp8_status_string.argtypes = [I]
         lib.mxfp8_status_string.restype = ctypes.c_char_p
         lib.mxfp8_version.argtypes = []
@@ -94,6 +96,11 @@ def fp8_block_scaled_gemm(M, N, K, a, lda, a_fmt, a_scales, b, ldb, b_fmt, b_lay
                           c, ldc, c_dtype, stream):
     return load_library().fp8_block_scaled_gemm(M, N, K, a, lda, a_fmt, a_scales, b, ldb, b_fmt, b_layout,
                                                  b_scales, b_scale_mode, c, ldc, c_dtype, stream)
+
+
+def mx_gemm(M, N, K, a, lda, a_fmt, a_scales, b, ldb, b_fmt, b_scales, c, ldc, c_dtype, stream):
+    return load_library().mx_gemm(M, N, K, a, lda, a_fmt, a_scales, b, ldb, b_fmt, b_scales, c, ldc, c_dtype,
+                                  stream)
 
 
 def mxfp8_status_string(status):
@@ -205,4 +212,20 @@ def block_scaled_gemm(a, a_scales, a_fmt, b, b_scales, b_fmt, b_layout=B_NK, b_s
                                b_fmt, b_layout, b_scales.data_ptr(), b_scale_mode, out.data_ptr(), _ld(out),
                                c_dtype, _stream(stream))
     _check(st, "fp8_block_scaled_gemm")
+    return out
+
+
+def mx_scaled_gemm(a, a_scales, a_fmt, b, b_scales, b_fmt, out_dtype=None, out=None, stream=None):
+    """C = A * B^T over MX codes: a [M][K], b [N][K], scales [rows][K/32] (quantize_mx's layout)."""
+    torch = _torch()
+    M, K = a.shape
+    N = b.shape[0]
+    if out is None:
+        dt = torch.float32 if out_dtype in (None, torch.float32) else torch.bfloat16
+        buf = torch.empty((M, _pad16(max(N, 1))), dtype=dt, device=a.device)
+        out = buf[:, :N]
+    c_dtype = F32 if out.dtype == torch.float32 else BF16
+    st = mx_gemm(M, N, K, a.data_ptr(), _ld(a), a_fmt, a_scales.data_ptr(), b.data_ptr(), _ld(b), b_fmt,
+                 b_scales.data_ptr(), out.data_ptr(), _ld(out), c_dtype, _stream(stream))
+    _check(st, "mx_gemm")
     return out

@@ -110,6 +110,34 @@ int fp8_block_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int
   return launch_status();
 }
 
+int mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, int a_fmt, const uint8_t* a_scales,
+            const uint8_t* b, int64_t ldb, int b_fmt, const uint8_t* b_scales, void* c, int64_t ldc, int c_dtype,
+            void* stream) {
+  if (a_fmt != MXFP8_E4M3 && a_fmt != MXFP8_E5M2) return MXFP8_ERR_ENUM;
+  if (b_fmt != MXFP8_E4M3 && b_fmt != MXFP8_E5M2) return MXFP8_ERR_ENUM;
+  if (c_dtype != MXFP8_F32 && c_dtype != MXFP8_BF16) return MXFP8_ERR_ENUM;
+  if (M < 0 || N < 0 || K < 0) return MXFP8_ERR_SHAPE;
+  if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return MXFP8_ERR_SHAPE;
+  if (K % 128 != 0) return MXFP8_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXFP8_OK;
+  if (!c) return MXFP8_ERR_NULL;
+  if (K > 0 && (!a || !a_scales || !b || !b_scales)) return MXFP8_ERR_NULL;
+  if (ldc < N || ldc % 16 != 0) return MXFP8_ERR_LD;
+  if (K > 0) {
+    if (lda < K || lda % 16 != 0) return MXFP8_ERR_LD;
+    if (ldb < K || ldb % 16 != 0) return MXFP8_ERR_LD;
+    if (!aligned16(a) || !aligned16(b)) return MXFP8_ERR_ALIGN;
+    if (((uintptr_t)a_scales & 3) || ((uintptr_t)b_scales & 3)) return MXFP8_ERR_ALIGN;
+  }
+  if (!aligned16(c)) return MXFP8_ERR_ALIGN;
+  if (c == (const void*)a || c == (const void*)b || c == (const void*)a_scales || c == (const void*)b_scales)
+    return MXFP8_ERR_ALIAS;
+  (void)hipGetLastError();
+  mxfp8::launch_mx_gemm(M, N, K, a, lda, a_fmt, a_scales, b, ldb, b_fmt, b_scales, c, ldc, c_dtype,
+                        (hipStream_t)stream);
+  return launch_status();
+}
+
 const char* mxfp8_status_string(int status) {
   switch (status) {
     case MXFP8_OK: return "ok";

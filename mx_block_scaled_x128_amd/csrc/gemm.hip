@@ -134,7 +134,10 @@ __device__ __forceinline__ void mfma_retire_pad() {
 #define MXFP8_GEMM_DS_SPAN 3
 #endif
 
-template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW>
+// MXS: MX operands -- scales per (row, 32-wide K block) for A ([M][K/32])
+// and for B stored [N][K] ([N][K/32]); otherwise one scale per 128-wide K
+// block (A [M][K/128]; B per row or per 128x128 tile of its storage).
+template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ SA,
     const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ SB, void* __restrict__ C,
@@ -142,6 +145,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int MT = WM / 32, NT = WN / 32;          // 32x32 MFMA tiles per wave
+  static_assert(!MXS || (!BKN && BROW), "MX scales: B stored [N][K], scales per row");
   // LDS: two K-block buffers, each holding both 64-wide stages of one
   // 128-wide K block: the A tile [BM][128 B] and the B tile ([BN][128 B], or
   // [128 k][BN B] when B is [K][N]).  Whole 128-byte rows per load
@@ -157,10 +161,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   static_assert(BM % 64 == 0 && BN % 64 == 0 && A_LOADS >= 1 && B_LOADS >= 1, "tile");
   static_assert(BM <= kThreads && BN <= kThreads, "one scale entity per lane quarter");
   static_assert(A_LOADS + B_LOADS + 8 <= 63, "vmcnt range");
-  // Scale groups: the scale bytes of 4 consecutive K blocks for each of 256
-  // tile rows (A) and columns (B), double-buffered.  Byte d = 4 e + s of a
-  // group area (one dword per byte: the LDS layout of 1-byte LDS-bound
-  // loads) holds entity e's scale for K block 4g + s.  Loading 4 K blocks
+  // Scale groups: the scales of 4 consecutive K blocks for each of 256 tile
+  // rows (A) and columns (B), double-buffered.  Dword d = 4 e + s of a group
+  // area holds entity e's scale for K block 4g + s: one byte, zero-extended
+  // (the LDS layout of 1-byte LDS-bound loads), or with MXS the four 32-wide
+  // block scales of that K block (one 4-byte load).  Loading 4 K blocks
   // at a time touches each row's scale line once per 4 K blocks instead of
   // once per K block (rows are nkb bytes apart in [rows][K/128] scales).
   constexpr int SG_OP = kThreads * 4 * 4;            // one operand's group area (bytes)
@@ -239,28 +244,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // Scale sources.  Group g's load instruction j of a wave (4 per operand)
   // covers entities e = 16 (4 wave + j) + (lane >> 2), K block 4g + (lane & 3)
   // (clamped to the last one; rows past M / N are clamped too).
-  const uint8_t* sa_base = uniform_opaque(SA + (int64_t)m0 * nkb);
-  const uint8_t* sb_base = uniform_opaque(BROW ? SB + (int64_t)n0 * nkb : SB);
+  const int srow = MXS ? 4 * nkb : nkb;  // scale bytes per row of A (and of per-row B scales)
+  const uint8_t* sa_base = uniform_opaque(SA + (int64_t)m0 * srow);
+  const uint8_t* sb_base = uniform_opaque(BROW ? SB + (int64_t)n0 * srow : SB);
   auto sdma_group = [&](int grp) __attribute__((always_inline)) {
     uint8_t* area = sgrp + (grp & 1) * SG;
     const int kbs = min(4 * grp + (lane & 3), nkb - 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = (wave * 4 + j) * 16 + (lane >> 2);
-      const uint32_t off = (uint32_t)(min(e, M - 1 - m0) * nkb + kbs);
-      __builtin_amdgcn_global_load_lds(sa_base + off, area + (wave * 4 + j) * 256, 1, 0, 0);
+      if (MXS) {
+        const uint32_t off = (uint32_t)(min(e, M - 1 - m0) * srow + 4 * kbs);
+        __builtin_amdgcn_global_load_lds(sa_base + off, area + (wave * 4 + j) * 256, 4, 0, 0);
+      } else {
+        const uint32_t off = (uint32_t)(min(e, M - 1 - m0) * nkb + kbs);
+        __builtin_amdgcn_global_load_lds(sa_base + off, area + (wave * 4 + j) * 256, 1, 0, 0);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = (wave * 4 + j) * 16 + (lane >> 2);
-      uint32_t off;
-      if (BROW) {
-        off = (uint32_t)(min(e, N - 1 - n0) * nkb + kbs);
+      if (MXS) {
+        const uint32_t off = (uint32_t)(min(e, N - 1 - n0) * srow + 4 * kbs);
+        __builtin_amdgcn_global_load_lds(sb_base + off, area + SG_OP + (wave * 4 + j) * 256, 4, 0, 0);
       } else {
-        const int nb = min((n0 + e) >> 7, nnb - 1);
-        off = (uint32_t)(BKN ? kbs * nnb + nb : nb * nkb + kbs);
+        uint32_t off;
+        if (BROW) {
+          off = (uint32_t)(min(e, N - 1 - n0) * nkb + kbs);
+        } else {
+          const int nb = min((n0 + e) >> 7, nnb - 1);
+          off = (uint32_t)(BKN ? kbs * nnb + nb : nb * nkb + kbs);
+        }
+        __builtin_amdgcn_global_load_lds(sb_base + off, area + SG_OP + (wave * 4 + j) * 256, 1, 0, 0);
       }
-      __builtin_amdgcn_global_load_lds(sb_base + off, area + SG_OP + (wave * 4 + j) * 256, 1, 0, 0);
     }
   };
 
@@ -291,15 +307,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
     for (int item = 0; item < DMA_ITEMS; ++item) dma_item(p, src, item);
   };
 
-  // Scale operands of K block kb (from its group's area).
-  const uint32_t sa_rd = opaque((wm * WM + (lane & 31)) * 16);
-  const uint32_t sb_rd = opaque(SG_OP + (wn * WN + (lane & 31)) * 16);
+  // Scale operands of K block kb (from its group's area).  With MXS, lane
+  // half g reads the 32-wide block scales 2g and 2g+1 of the K block (the
+  // chunks whose scale it supplies in the block's two stages, see below);
+  // stage h selects byte h with the MFMA's operand select.
+  const int g = lane >> 5;
+  const uint32_t sa_rd = opaque((wm * WM + (lane & 31)) * 16 + (MXS ? 2 * g : 0));
+  const uint32_t sb_rd = opaque(SG_OP + (wn * WN + (lane & 31)) * 16 + (MXS ? 2 * g : 0));
   auto read_scales = [&](int kb, int (&sa)[MT], int (&sb)[NT]) __attribute__((always_inline)) {
     const uint8_t* area = sgrp + ((kb >> 2) & 1) * SG + (kb & 3) * 4;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) sa[mt] = *reinterpret_cast<const int*>(area + sa_rd + mt * 512);
+    for (int mt = 0; mt < MT; ++mt)
+      sa[mt] = MXS ? (int)*reinterpret_cast<const uint16_t*>(area + sa_rd + mt * 512)
+                   : *reinterpret_cast<const int*>(area + sa_rd + mt * 512);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sb[nt] = *reinterpret_cast<const int*>(area + sb_rd + nt * 512);
+    for (int nt = 0; nt < NT; ++nt)
+      sb[nt] = MXS ? (int)*reinterpret_cast<const uint16_t*>(area + sb_rd + nt * 512)
+                   : *reinterpret_cast<const int*>(area + sb_rd + nt * 512);
   };
 
   v16f acc[MT][NT];
@@ -310,10 +334,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.0f;
 
-  const int g = lane >> 5;
   // Fragments of one 64-wide stage (half h of a K block).  Lane l holds, for
-  // its row (A) / column (B) l & 31, bytes k = 32*(l>>5) .. +31 of the stage,
-  // in k order, for both operands (the pairing the MFMA needs).  One LDS read
+  // its row (A) / column (B) l & 31, 32 K bytes as two 16-byte parts (its
+  // first and last four registers), for both operands (the pairing the MFMA
+  // needs).  The matrix core's own K order: lane half g = l >> 5 holds k
+  // 16 g .. +15 in part 0 and 32 + 16 g .. +15 in part 1, and with scales per
+  // 32 k the first 32 (part 0 of both halves) take the scale of lanes 0-31,
+  // the last 32 that of lanes 32-63 (measured: a product placed in part 1 of
+  // half 0 is scaled by the upper lanes' byte).  With MXS, stage h puts the
+  // K block's 32-wide chunk h in part 0 and chunk 2 + h in part 1, so lane
+  // half g's scales over the two stages are chunks 2g and 2g + 1: adjacent
+  // bytes, one 16-bit read.  Without MXS (one scale per 128-wide block) any
+  // K order shared by A and B gives the same sums; stage h then takes bytes
+  // 64 h .. +63.  One LDS read
   // per item: A items 2*mt + part (16 bytes each), then B items (two 16-byte
   // parts per fragment, or four 8-byte transposed parts when B is [K][N]).
   constexpr int B_PARTS = BKN ? 4 : 2;
@@ -328,7 +361,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
 #pragma unroll
     for (int part = 0; part < 2; ++part) {
       const int r = wm * WM + (lane & 31);
-      a_rd[h][part] = opaque(r * KBB + (((4 * h + 2 * g + part) ^ swz128(r)) << 4));
+      const int unit = MXS ? 4 * part + 2 * h + g : 4 * h + 2 * g + part;  // 16-byte unit of the row
+      a_rd[h][part] = opaque(r * KBB + ((unit ^ swz128(r)) << 4));
     }
   if (!BKN) {
 #pragma unroll
@@ -336,7 +370,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
 #pragma unroll
       for (int part = 0; part < 2; ++part) {
         const int r = wn * WN + (lane & 31);
-        b_rd[h][part] = opaque(A_ST + r * KBB + (((4 * h + 2 * g + part) ^ swz128(r)) << 4));
+        const int unit = MXS ? 4 * part + 2 * h + g : 4 * h + 2 * g + part;
+        b_rd[h][part] = opaque(A_ST + r * KBB + ((unit ^ swz128(r)) << 4));
       }
   } else {
     // 16-lane group grp covers columns 16*(grp&1) .. +15 and k half grp>>1;
@@ -392,7 +427,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // rd_p >= 0: read the fragments of stage half rd_h of buffer rd_p into
   // (na, nb); with do_sc also K block sc_kb's scales into (nsa, nsb).
   // grp >= 0: load scale group grp.
-  auto stage = [&](int dma_p, int dma_kb, int rd_p, int rd_h, bool do_sc, int sc_kb, int grp, const v8i (&ca)[MT],
+  auto stage = [&](int cur_h, int dma_p, int dma_kb, int rd_p, int rd_h, bool do_sc, int sc_kb, int grp,
+                   const v8i (&ca)[MT],
                    const v8i (&cb)[NT], v8i (&na)[MT], v8i (&nb)[NT], const int (&csa)[MT],
                    const int (&csb)[NT], int (&nsa)[MT], int (&nsb)[NT]) __attribute__((always_inline)) {
     Src src = {nullptr, nullptr};
@@ -400,8 +436,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
 #pragma unroll
     for (int i = 0; i < MFMAS; ++i) {
       const int mt = i / NT, nt = i % NT;
-      acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[nt], ca[mt], acc[mt][nt], BFMT, AFMT, 0,
-                                                                   csb[nt], 0, csa[mt]);
+      if (MXS && cur_h == 1)
+        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[nt], ca[mt], acc[mt][nt], BFMT, AFMT, 1,
+                                                                     csb[nt], 1, csa[mt]);
+      else
+        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[nt], ca[mt], acc[mt][nt], BFMT, AFMT, 0,
+                                                                     csb[nt], 0, csa[mt]);
       if (rd_p >= 0 && do_sc && i == 0) read_scales(sc_kb, nsa, nsb);
       if (grp >= 0 && i == 0) sdma_group(grp);  // after the scale read: same array
 #pragma unroll
@@ -436,9 +476,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // bytes nobody reads.  A group is read from 2 to 3 K blocks later on.
   auto kblock = [&](int p, int kb, bool dma, bool next, bool sg, const int (&csa)[MT], const int (&csb)[NT],
                     int (&nsa)[MT], int (&nsb)[NT]) __attribute__((always_inline)) {
-    stage(-1, 0, p, 1, false, 0, -1, fa0, fb0, fa1, fb1, csa, csb, nsa, nsb);
+    stage(0, -1, 0, p, 1, false, 0, -1, fa0, fb0, fa1, fb1, csa, csb, nsa, nsb);
     if (dma || next) wait_vm_barrier<0>();
-    stage(dma ? p : -1, kb + 2, next ? (p ^ 1) : -1, 0, next, kb + 1, sg ? (kb >> 2) + 1 : -1, fa1, fb1, fa0,
+    stage(1, dma ? p : -1, kb + 2, next ? (p ^ 1) : -1, 0, next, kb + 1, sg ? (kb >> 2) + 1 : -1, fa1, fb1, fa0,
           fb0, csa, csb, nsa, nsb);
   };
 
@@ -594,12 +634,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
 #endif
 }
 
-template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW>
+template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS>
 void launch_tile(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
                  const uint8_t* b, int64_t ldb, const uint8_t* sb, void* c, int64_t ldc, int c_dtype,
                  int tiles_m, int tiles_n, int tile_first, int cells, int split, hipStream_t stream) {
   if (cells <= 0) return;
-  hipLaunchKernelGGL((gemm_bs_kernel<BM, BN, STAGES, AFMT, BFMT, BKN, BROW>), dim3(cells << (2 * split)),
+  hipLaunchKernelGGL((gemm_bs_kernel<BM, BN, STAGES, AFMT, BFMT, BKN, BROW, MXS>), dim3(cells << (2 * split)),
                      dim3(kThreads), 0, stream, (int)M, (int)N, (int)K, a, lda, sa, b, ldb, sb, c, ldc,
                      c_dtype == 1 ? 1 : 0, tiles_m, tiles_n, tile_first, split);
 }
@@ -624,7 +664,7 @@ int device_cus() {
 #ifndef MXFP8_GEMM_TILE
 #define MXFP8_GEMM_TILE 0
 #endif
-template <int AFMT, int BFMT, bool BKN, bool BROW>
+template <int AFMT, int BFMT, bool BKN, bool BROW, bool MXS>
 void launch_shape(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
                   const uint8_t* b, int64_t ldb, const uint8_t* sb, void* c, int64_t ldc, int c_dtype,
                   hipStream_t stream) {
@@ -635,7 +675,7 @@ void launch_shape(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda
   const bool big = K >= 256 && (MXFP8_GEMM_TILE == 256 || (MXFP8_GEMM_TILE == 0 && big_tiles >= cus));
   if (!big) {
     const int sm = (int)((M + 127) / 128), sn = (int)((N + 127) / 128);
-    launch_tile<128, 128, 4, AFMT, BFMT, BKN, BROW>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, sm, sn, 0,
+    launch_tile<128, 128, 4, AFMT, BFMT, BKN, BROW, MXS>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, sm, sn, 0,
                                                     sm * sn, 0, stream);
     return;
   }
@@ -644,10 +684,10 @@ void launch_shape(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda
   const int tail = big_tiles % cus;
   const bool split_tail = MXFP8_GEMM_TILE == 0 && big_tiles > cus && tail > 0 && 4 * tail <= cus;
   const int main_cells = split_tail ? big_tiles - tail : big_tiles;
-  launch_tile<256, 256, 4, AFMT, BFMT, BKN, BROW>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, bm, bn, 0,
+  launch_tile<256, 256, 4, AFMT, BFMT, BKN, BROW, MXS>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, bm, bn, 0,
                                                   main_cells, 0, stream);
   if (split_tail)
-    launch_tile<128, 128, 4, AFMT, BFMT, BKN, BROW>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, bm, bn,
+    launch_tile<128, 128, 4, AFMT, BFMT, BKN, BROW, MXS>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, bm, bn,
                                                     main_cells, tail, 1, stream);
 }
 
@@ -656,11 +696,11 @@ void launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, 
                 const uint8_t* b, int64_t ldb, int b_layout, const uint8_t* sb, int b_scale_mode, void* c,
                 int64_t ldc, int c_dtype, hipStream_t stream) {
   if (b_layout == 1)
-    launch_shape<AFMT, BFMT, true, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+    launch_shape<AFMT, BFMT, true, false, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
   else if (b_scale_mode == 1)
-    launch_shape<AFMT, BFMT, false, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+    launch_shape<AFMT, BFMT, false, true, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
   else
-    launch_shape<AFMT, BFMT, false, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+    launch_shape<AFMT, BFMT, false, false, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
 }
 
 }  // namespace gemm_detail
@@ -679,6 +719,19 @@ void launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
     launch_fmt<0, 1>(M, N, K, a, lda, sa, b, ldb, b_layout, sb, b_scale_mode, c, ldc, c_dtype, stream);
   else
     launch_fmt<1, 1>(M, N, K, a, lda, sa, b, ldb, b_layout, sb, b_scale_mode, c, ldc, c_dtype, stream);
+}
+
+void launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, int a_fmt,
+                    const uint8_t* sa, const uint8_t* b, int64_t ldb, int b_fmt, const uint8_t* sb, void* c,
+                    int64_t ldc, int c_dtype, hipStream_t stream) {
+  if (a_fmt == 0 && b_fmt == 0)
+    launch_shape<0, 0, false, true, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+  else if (a_fmt == 1 && b_fmt == 0)
+    launch_shape<1, 0, false, true, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+  else if (a_fmt == 0 && b_fmt == 1)
+    launch_shape<0, 1, false, true, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+  else
+    launch_shape<1, 1, false, true, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
 }
 
 }  // namespace mxfp8

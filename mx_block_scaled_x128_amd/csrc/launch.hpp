@@ -25,4 +25,10 @@ void launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
                  const uint8_t* sb, int b_scale_mode, void* c, int64_t ldc, int c_dtype,
                  hipStream_t stream);
 
+// MX GEMM: A [M][K] with scales [M][K/32], B [N][K] with scales [N][K/32].
+// K % 128 == 0, M, N >= 1, scale pointers 4-byte aligned.
+void launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, int a_fmt,
+                    const uint8_t* sa, const uint8_t* b, int64_t ldb, int b_fmt, const uint8_t* sb, void* c,
+                    int64_t ldc, int c_dtype, hipStream_t stream);
+
 }  // namespace mxfp8

@@ -26,7 +26,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = mx.load_library()
     names = declared_functions()
     assert set(names) >= {"fp8_quantize_token", "fp8_quantize_block", "mx_quantize", "fp8_block_scaled_gemm",
-                          "mxfp8_status_string", "mxfp8_version"}
+                          "mx_gemm", "mxfp8_status_string", "mxfp8_version"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -103,6 +103,21 @@ def test_gemm_validation():
     assert gemm(blay=1, ldb=128) == LD  # KN: ldb >= N
     assert gemm(a=MIS) == ALIGN and gemm(c=MIS) == ALIGN
     assert gemm(c=X) == ALIAS and gemm(c=S) == ALIAS
+
+
+def mxg(M=256, N=256, K=512, a=X, lda=512, afmt=0, sa=S, b=Q, ldb=512, bfmt=0, sb=P2, c=C, ldc=256, cdt=0):
+    return mx.mx_gemm(M, N, K, a, lda, afmt, sa, b, ldb, bfmt, sb, c, ldc, cdt, None)
+
+
+def test_mx_gemm_validation():
+    assert mxg(afmt=2) == ENUM and mxg(bfmt=-1) == ENUM and mxg(cdt=2) == ENUM
+    assert mxg(K=480) == SHAPE and mxg(K=32) == SHAPE and mxg(N=-1) == SHAPE and mxg(M=2 ** 31) == SHAPE
+    assert mxg(M=0, a=None, sa=None) == OK and mxg(N=0, c=None) == OK
+    assert mxg(c=None) == NULL and mxg(b=None) == NULL and mxg(sa=None) == NULL and mxg(sb=None) == NULL
+    assert mxg(lda=496) == LD and mxg(ldb=520) == LD and mxg(ldc=255) == LD
+    assert mxg(a=MIS) == ALIGN and mxg(c=MIS) == ALIGN
+    assert mxg(sa=S + 2) == ALIGN and mxg(sb=P2 + 1) == ALIGN
+    assert mxg(c=X) == ALIAS and mxg(c=Q) == ALIAS and mxg(c=S) == ALIAS and mxg(c=P2) == ALIAS
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

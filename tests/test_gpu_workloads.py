@@ -97,6 +97,26 @@ def test_mx_stress_tensor(j, golden):
     assert cnt[:2048].sum() == 0  # 1 + N(0, 1e-3) rows sit just above a power of two
 
 
+def test_mx_fprop_1p5b():
+    """The fprop GEMM on MX operands: activations [4096][1536] and weights
+    [8960][1536] quantized with 32-element E8M0 scales (OCP floor rule), bf16
+    output; quantizers compared in full, the GEMM on samples at the plain bound."""
+    d = synth.fprop1p5b()
+    xq, xs, _ = mx.quantize_mx(dev(d["x"]), mx.E4M3, mx.RULE_FLOOR, counts=False)
+    wq, ws, _ = mx.quantize_mx(dev(d["w"]), mx.E4M3, mx.RULE_FLOOR, counts=False)
+    y = mx.mx_scaled_gemm(xq, xs, mx.E4M3, wq, ws, mx.E4M3, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    xq_ref, xs_ref, _ = oracle.mx_quantize(d["x"], oracle.E4M3, oracle.RULE_FLOOR, threads=ORACLE_THREADS)
+    wq_ref, ws_ref, _ = oracle.mx_quantize(d["w"], oracle.E4M3, oracle.RULE_FLOOR, threads=ORACLE_THREADS)
+    assert np.array_equal(host(xs), xs_ref) and np.array_equal(host(xq), xq_ref)
+    assert np.array_equal(host(ws), ws_ref) and np.array_equal(host(wq), wq_ref)
+    yh = host(y)
+    assert np.isfinite(yh).all()
+    ii, jj = sample_points(*yh.shape, 55)
+    y_ref, t_ref = oracle.mx_gemm_elems(xq_ref, xs_ref, 0, wq_ref, ws_ref, 0, ii, jj, threads=ORACLE_THREADS)
+    assert_gemm_close(yh[ii, jj], y_ref, t_ref, True, "mx fprop bf16")
+
+
 def test_wgrad():
     d = synth.wgrad()
     xq, xs = mx.quantize_token(dev(d["x"]), mx.E4M3, mx.COL_T)     # [4096][16384], [4096][128]
