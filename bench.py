@@ -14,8 +14,9 @@ entry point is timed with events on the stream it runs on, and the dominant
 one (the GEMM) is reported against the dense FP8 MFMA peak.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 
-Other workloads (--workload): dgrad7b, wgrad, mxstress -- for the per-kernel
-roofline figures; they print the same kind of JSON line.
+Other workloads (--workload): dgrad7b, wgrad, mxfprop1p5b (the fprop step on
+MX operands: 32-element E8M0 scales for X and W, mx_gemm), mxstress -- for
+the per-kernel roofline figures; they print the same kind of JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 """
@@ -38,7 +39,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="fprop1p5b",
-                   choices=["fprop1p5b", "dgrad7b", "wgrad", "mxstress", "copy"])
+                   choices=["fprop1p5b", "dgrad7b", "wgrad", "mxfprop1p5b", "mxstress", "copy"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=0,
                    help="token rows in the oracle sample (0 = all rows: the full step)")
@@ -322,6 +323,32 @@ def bench_other(args):
         flops = 2.0 * M * N * K
         desc = "wgrad: column-quantize X and dY 16384x4096 bf16 along tokens (E4M3 / E5M2) + GEMM M=N=4096 " \
                "K=16384 fp32 out"
+    elif args.workload == "mxfprop1p5b":
+        d = synth.fprop1p5b()
+        x, w = to_dev(d["x"]), to_dev(d["w"])
+        del d
+        M, K = x.shape
+        N = w.shape[0]
+        xq, xs = torch.empty((M, K), **u8), torch.empty((M, K // 32), **u8)
+        wq, ws = torch.empty((N, K), **u8), torch.empty((N, K // 32), **u8)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+        def step(timer):
+            stream = cur()
+            _check(timer.run("mx_quant_x", lambda: mx.mx_quantize(
+                x.data_ptr(), mx.BF16, M, K, K, mx.E4M3, mx.RULE_FLOOR, xq.data_ptr(), K, xs.data_ptr(), None,
+                stream)), "mx")
+            _check(timer.run("mx_quant_w", lambda: mx.mx_quantize(
+                w.data_ptr(), mx.BF16, N, K, K, mx.E4M3, mx.RULE_FLOOR, wq.data_ptr(), K, ws.data_ptr(), None,
+                stream)), "mx")
+            _check(timer.run("gemm", lambda: mx.mx_gemm(
+                M, N, K, xq.data_ptr(), K, mx.E4M3, xs.data_ptr(), wq.data_ptr(), K, mx.E4M3, ws.data_ptr(),
+                y.data_ptr(), N, mx.BF16, stream)), "gemm")
+        sizes = {"mx_quant_x": M * K * 3 + M * K // 32, "mx_quant_w": N * K * 3 + N * K // 32}
+        outputs = [xq, xs, wq, ws, y]
+        flops = 2.0 * M * N * K
+        desc = "mxfprop1p5b: MX-quantize X 4096x1536 and W 8960x1536 bf16 (32-element E4M3 blocks, OCP floor " \
+               "scales) + MX GEMM M=4096 N=8960 K=1536 bf16 out"
     else:
         xs_ = [to_dev(synth.mxstress_tensor(j)) for j in range(64)]
         R, C = xs_[0].shape
