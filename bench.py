@@ -15,8 +15,10 @@ one (the GEMM) is reported against the dense FP8 MFMA peak.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 
 Other workloads (--workload): dgrad7b, wgrad, mxfprop1p5b (the fprop step on
-MX operands: 32-element E8M0 scales for X and W, mx_gemm), mxstress -- for
-the per-kernel roofline figures; they print the same kind of JSON line.
+MX operands: 32-element E8M0 scales for X and W, mx_gemm), dualq (the
+two-orientation quantizers on the wgrad activation and the dgrad weight),
+mxstress -- for the per-kernel roofline figures; they print the same kind of
+JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 """
@@ -39,7 +41,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="fprop1p5b",
-                   choices=["fprop1p5b", "dgrad7b", "wgrad", "mxfprop1p5b", "mxstress", "copy"])
+                   choices=["fprop1p5b", "dgrad7b", "wgrad", "mxfprop1p5b", "dualq", "mxstress", "copy"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=0,
                    help="token rows in the oracle sample (0 = all rows: the full step)")
@@ -349,6 +351,31 @@ def bench_other(args):
         flops = 2.0 * M * N * K
         desc = "mxfprop1p5b: MX-quantize X 4096x1536 and W 8960x1536 bf16 (32-element E4M3 blocks, OCP floor " \
                "scales) + MX GEMM M=4096 N=8960 K=1536 bf16 out"
+    elif args.workload == "dualq":
+        x = to_dev(synth.wgrad()["x"])
+        w = to_dev(synth.dgrad7b(rows=16)["w"])
+        T, C = x.shape
+        O, I = w.shape
+        xq, xs = torch.empty((T, C), **u8), torch.empty((T, C // 128), **u8)
+        xqt, xst = torch.empty((C, T), **u8), torch.empty((C, T // 128), **u8)
+        wq, ws = torch.empty((O, I), **u8), torch.empty(((O + 127) // 128, I // 128), **u8)
+        wqt, wst = torch.empty((I, O), **u8), torch.empty((I // 128, (O + 127) // 128), **u8)
+
+        def step(timer):
+            stream = cur()
+            _check(timer.run("token_dual_x", lambda: mx.fp8_quantize_token_dual(
+                x.data_ptr(), mx.BF16, T, C, C, mx.E4M3, xq.data_ptr(), C, xs.data_ptr(), xqt.data_ptr(), T,
+                xst.data_ptr(), stream)), "dual")
+            _check(timer.run("block_dual_w", lambda: mx.fp8_quantize_block_dual(
+                w.data_ptr(), mx.BF16, O, I, I, mx.E4M3, wq.data_ptr(), I, ws.data_ptr(), wqt.data_ptr(), O,
+                wst.data_ptr(), stream)), "dual")
+        sizes = {"token_dual_x": T * C * 4 + 2 * T * C // 128,
+                 "block_dual_w": O * I * 4 + 2 * ((O + 127) // 128) * (I // 128)}
+        outputs = [xq, xs, xqt, xst, wq, ws, wqt, wst]
+        flops = 0.0
+        M = N = K = 0
+        desc = "dualq: X 16384x4096 bf16 -> 1x128 row codes + 128-token column codes (transposed), one read; " \
+               "W 18944x3584 bf16 -> 128x128 block codes + their transpose"
     else:
         xs_ = [to_dev(synth.mxstress_tensor(j)) for j in range(64)]
         R, C = xs_[0].shape
@@ -379,10 +406,11 @@ def bench_other(args):
         roof = {"bound": "mfma", "achieved": round(flops / g / 1e12, 2), "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(flops / g / 1e12 / FP8_PEAK_TFLOPS, 4), "traffic": None}
     else:
-        tot = sum(sizes.values()) * 64
+        tot = sum(sizes.values()) * (64 if args.workload == "mxstress" else 1)
         value, unit = tot / per_step / 1e9, "GB/s"
-        roof = {"bound": "hbm", "achieved": kern["mx_quant"]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": kern["mx_quant"]["frac_hbm_peak"], "traffic": None}
+        dom = max(sizes, key=lambda k: kern[k]["us"])
+        roof = {"bound": "hbm", "achieved": kern[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": kern[dom]["frac_hbm_peak"], "traffic": None, "kernel": dom}
     return {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(per_step * 1e3, 4),

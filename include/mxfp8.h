@@ -114,6 +114,37 @@ int fp8_quantize_block(const void* w, int w_dtype, int64_t rows, int64_t cols, i
                        int fmt, uint8_t* q, int64_t ldq, uint8_t* scales, void* stream);
 
 /*
+ * fp8_quantize_token_dual -- both orientations of fp8_quantize_token from one
+ * read of x: the ROW groups that the forward GEMM consumes and the transposed
+ * COL_T groups that the weight-gradient GEMM consumes [INFR "What carries the
+ * argument", Fig. 2: one tensor quantized token-wise feeds the forward and
+ * the backward GEMMs].  The outputs are byte-for-byte those of the two
+ * one-orientation calls:
+ *   q:        [rows][ldq >= cols],  scales:   [rows][ceil(cols / 128)]  (ROW);
+ *   qt:       [cols][ldqt >= rows], scales_t: [cols][ceil(rows / 128)]  (COL_T).
+ * Requires rows % 16 == 0 and cols % 16 == 0; the four outputs are distinct.
+ */
+int fp8_quantize_token_dual(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                            int fmt, uint8_t* q, int64_t ldq, uint8_t* scales, uint8_t* qt,
+                            int64_t ldqt, uint8_t* scales_t, void* stream);
+
+/*
+ * fp8_quantize_block_dual -- fp8_quantize_block plus the transposed codes
+ * [INFR "What carries the argument", Fig. 1: 128x128 weight blocks serve the
+ * forward and the input-gradient GEMMs].  A tile has one scale, so its
+ * transpose holds the same bytes:
+ *   q:        [rows][ldq >= cols],  scales:   [ceil(rows/128)][ceil(cols/128)];
+ *   qt:       [cols][ldqt >= rows], scales_t: [ceil(cols/128)][ceil(rows/128)]
+ *             (qt[c * ldqt + r] = q[r * ldq + c]; scales_t is scales
+ *             transposed), so a GEMM can read w^T as an [N][K] operand with
+ *             MXFP8_SCALE_BLOCK128 scales.
+ * Requires rows % 16 == 0 and cols % 16 == 0; the four outputs are distinct.
+ */
+int fp8_quantize_block_dual(const void* w, int w_dtype, int64_t rows, int64_t cols, int64_t ldw,
+                            int fmt, uint8_t* q, int64_t ldq, uint8_t* scales, uint8_t* qt,
+                            int64_t ldqt, uint8_t* scales_t, void* stream);
+
+/*
  * mx_quantize -- MX quantization, 32 consecutive elements of a row sharing
  * one E8M0 scale [MXTI "What carries the argument", Fig. 5].
  *

@@ -7,10 +7,12 @@ stream; nothing here computes.  If the library has not been built, every
 entry point raises -- there is no fallback path.
 
 Low-level entry points carry the C names and signatures (pointers as ints):
-  fp8_quantize_token, fp8_quantize_block, mx_quantize, fp8_block_scaled_gemm,
-  mx_gemm, mxfp8_status_string, mxfp8_version.
+  fp8_quantize_token, fp8_quantize_block, fp8_quantize_token_dual,
+  fp8_quantize_block_dual, mx_quantize, fp8_block_scaled_gemm, mx_gemm,
+  mxfp8_status_string, mxfp8_version.
 Tensor conveniences allocate outputs with torch and call them:
-  quantize_token, quantize_block, quantize_mx, block_scaled_gemm, mx_scaled_gemm.
+  quantize_token, quantize_block, quantize_token_dual, quantize_block_dual,
+  quantize_mx, block_scaled_gemm, mx_scaled_gemm.
 """
 import ctypes
 import os
@@ -19,9 +21,10 @@ import threading
 __all__ = [
     "E4M3", "E5M2", "F32", "BF16", "ROW", "COL_T", "RULE_CEIL", "RULE_FLOOR", "B_NK", "B_KN",
     "SCALE_BLOCK128", "SCALE_ROW128", "MxFp8Error", "library_path", "load_library",
-    "fp8_quantize_token", "fp8_quantize_block", "mx_quantize", "fp8_block_scaled_gemm", "mx_gemm",
-    "mxfp8_status_string", "mxfp8_version",
-    "quantize_token", "quantize_block", "quantize_mx", "block_scaled_gemm", "mx_scaled_gemm",
+    "fp8_quantize_token", "fp8_quantize_block", "fp8_quantize_token_dual", "fp8_quantize_block_dual",
+    "mx_quantize", "fp8_block_scaled_gemm", "mx_gemm", "mxfp8_status_string", "mxfp8_version",
+    "quantize_token", "quantize_block", "quantize_token_dual", "quantize_block_dual", "quantize_mx",
+    "block_scaled_gemm", "mx_scaled_gemm",
 ]
 
 # enum values of include/mxfp8.h
@@ -63,6 +66,10 @@ def load_library():
         lib.fp8_quantize_token.restype = I
         lib.fp8_quantize_block.argtypes = [P, I, I64, I64, I64, I, P, I64, P, P]
         lib.fp8_quantize_block.restype = I
+        lib.fp8_quantize_token_dual.argtypes = [P, I, I64, I64, I64, I, P, I64, P, P, I64, P, P]
+        lib.fp8_quantize_token_dual.restype = I
+        lib.fp8_quantize_block_dual.argtypes = [P, I, I64, I64, I64, I, P, I64, P, P, I64, P, P]
+        lib.fp8_quantize_block_dual.restype = I
         lib.mx_quantize.argtypes = [P, I, I64, I64, I64, I, I, P, I64, P, P, P]
         lib.mx_quantize.restype = I
         lib.fp8_block_scaled_gemm.argtypes = [I64, I64, I64, P, I64, I, P, P, I64, I, I, P, I, P, I64, I, P]
@@ -85,6 +92,16 @@ def fp8_quantize_token(x, x_dtype, rows, cols, ldx, axis, fmt, q, ldq, scales, s
 
 def fp8_quantize_block(w, w_dtype, rows, cols, ldw, fmt, q, ldq, scales, stream):
     return load_library().fp8_quantize_block(w, w_dtype, rows, cols, ldw, fmt, q, ldq, scales, stream)
+
+
+def fp8_quantize_token_dual(x, x_dtype, rows, cols, ldx, fmt, q, ldq, scales, qt, ldqt, scales_t, stream):
+    return load_library().fp8_quantize_token_dual(x, x_dtype, rows, cols, ldx, fmt, q, ldq, scales, qt, ldqt,
+                                                  scales_t, stream)
+
+
+def fp8_quantize_block_dual(w, w_dtype, rows, cols, ldw, fmt, q, ldq, scales, qt, ldqt, scales_t, stream):
+    return load_library().fp8_quantize_block_dual(w, w_dtype, rows, cols, ldw, fmt, q, ldq, scales, qt, ldqt,
+                                                  scales_t, stream)
 
 
 def mx_quantize(x, x_dtype, rows, cols, ldx, fmt, rule, q, ldq, scales, clamp_counts, stream):
@@ -182,6 +199,35 @@ def quantize_block(w, fmt=E4M3, stream=None):
                             s.data_ptr(), _stream(stream))
     _check(st, "fp8_quantize_block")
     return q, s
+
+
+def quantize_token_dual(x, fmt=E4M3, stream=None):
+    """Both token orientations from one read: (q, scales) as quantize_token ROW and
+    (qt, scales_t) as quantize_token COL_T."""
+    torch = _torch()
+    rows, cols = x.shape
+    q = _codes(rows, cols, x.device)
+    s = torch.empty((rows, (cols + 127) // 128), dtype=torch.uint8, device=x.device)
+    qt = _codes(cols, rows, x.device)
+    st = torch.empty((cols, (rows + 127) // 128), dtype=torch.uint8, device=x.device)
+    r = fp8_quantize_token_dual(x.data_ptr(), _in_dtype(x), rows, cols, _ld(x), fmt, q.data_ptr(), _ld(q),
+                                s.data_ptr(), qt.data_ptr(), _ld(qt), st.data_ptr(), _stream(stream))
+    _check(r, "fp8_quantize_token_dual")
+    return q, s, qt, st
+
+
+def quantize_block_dual(w, fmt=E4M3, stream=None):
+    """128x128 block quantization with the transposed codes: (q, scales, qt, scales_t)."""
+    torch = _torch()
+    rows, cols = w.shape
+    q = _codes(rows, cols, w.device)
+    s = torch.empty(((rows + 127) // 128, (cols + 127) // 128), dtype=torch.uint8, device=w.device)
+    qt = _codes(cols, rows, w.device)
+    st = torch.empty(((cols + 127) // 128, (rows + 127) // 128), dtype=torch.uint8, device=w.device)
+    r = fp8_quantize_block_dual(w.data_ptr(), _in_dtype(w), rows, cols, _ld(w), fmt, q.data_ptr(), _ld(q),
+                                s.data_ptr(), qt.data_ptr(), _ld(qt), st.data_ptr(), _stream(stream))
+    _check(r, "fp8_quantize_block_dual")
+    return q, s, qt, st
 
 
 def quantize_mx(x, fmt=E4M3, rule=RULE_FLOOR, counts=True, stream=None):

@@ -64,6 +64,44 @@ int fp8_quantize_block(const void* w, int w_dtype, int64_t rows, int64_t cols, i
   return launch_status();
 }
 
+namespace {
+// Checks shared by the two-orientation quantizers: both output pairs as for
+// the one-orientation calls, both extents multiples of 16, four distinct outputs.
+int check_dual(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt, const uint8_t* q,
+               int64_t ldq, const uint8_t* s, const uint8_t* qt, int64_t ldqt, const uint8_t* st) {
+  if (fmt != MXFP8_E4M3 && fmt != MXFP8_E5M2) return MXFP8_ERR_ENUM;
+  int r = check_tensor_pair(x, dtype, rows, cols, ldx, q, ldq, cols, s);
+  if (r != MXFP8_OK || rows == 0 || cols == 0) return r;
+  r = check_tensor_pair(x, dtype, rows, cols, ldx, qt, ldqt, rows, st);
+  if (r != MXFP8_OK) return r;
+  if (cols % 16 != 0 || rows % 16 != 0) return MXFP8_ERR_SHAPE;
+  if (q == qt || q == st || s == qt || s == st) return MXFP8_ERR_ALIAS;
+  return MXFP8_OK;
+}
+}  // namespace
+
+int fp8_quantize_token_dual(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                            uint8_t* q, int64_t ldq, uint8_t* scales, uint8_t* qt, int64_t ldqt,
+                            uint8_t* scales_t, void* stream) {
+  const int st = check_dual(x, x_dtype, rows, cols, ldx, fmt, q, ldq, scales, qt, ldqt, scales_t);
+  if (st != MXFP8_OK || rows == 0 || cols == 0) return st;
+  (void)hipGetLastError();
+  mxfp8::launch_quant_dual(x, x_dtype, rows, cols, ldx, fmt, q, ldq, scales, qt, ldqt, scales_t,
+                           (hipStream_t)stream);
+  return launch_status();
+}
+
+int fp8_quantize_block_dual(const void* w, int w_dtype, int64_t rows, int64_t cols, int64_t ldw, int fmt,
+                            uint8_t* q, int64_t ldq, uint8_t* scales, uint8_t* qt, int64_t ldqt,
+                            uint8_t* scales_t, void* stream) {
+  const int st = check_dual(w, w_dtype, rows, cols, ldw, fmt, q, ldq, scales, qt, ldqt, scales_t);
+  if (st != MXFP8_OK || rows == 0 || cols == 0) return st;
+  (void)hipGetLastError();
+  mxfp8::launch_quant_block_dual(w, w_dtype, rows, cols, ldw, fmt, q, ldq, scales, qt, ldqt, scales_t,
+                                 (hipStream_t)stream);
+  return launch_status();
+}
+
 int mx_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt, int rule,
                 uint8_t* q, int64_t ldq, uint8_t* scales, uint8_t* clamp_counts, void* stream) {
   if (fmt != MXFP8_E4M3 && fmt != MXFP8_E5M2) return MXFP8_ERR_ENUM;

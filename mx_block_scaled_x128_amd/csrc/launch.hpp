@@ -16,6 +16,15 @@ void launch_quant_col_t(const void* x, int dtype, int64_t rows, int64_t cols, in
 // 128x128 tiles.  cols % 16 == 0.
 void launch_quant_block(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw, int fmt,
                         uint8_t* q, int64_t ldq, uint8_t* s, hipStream_t stream);
+// Both token orientations from one read: row groups (q, s) and transposed
+// column groups (qt, st).  rows % 16 == 0, cols % 16 == 0.
+void launch_quant_dual(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
+                       int64_t ldq, uint8_t* s, uint8_t* qt, int64_t ldqt, uint8_t* st, hipStream_t stream);
+// 128x128 tiles, codes and transposed codes; s [rows/128][cols/128], st its transpose.
+// rows % 16 == 0, cols % 16 == 0.
+void launch_quant_block_dual(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw, int fmt,
+                             uint8_t* q, int64_t ldq, uint8_t* s, uint8_t* qt, int64_t ldqt, uint8_t* st,
+                             hipStream_t stream);
 // 32-element MX blocks along rows.  cols % 32 == 0.
 void launch_mx(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt, int rule,
                uint8_t* q, int64_t ldq, uint8_t* s, uint8_t* counts, hipStream_t stream);

@@ -152,6 +152,196 @@ __global__ __launch_bounds__(kThreads) void quant_col_t_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Both orientations of the token-wise quantization from one read of x: the
+// 1x128 row groups (codes in x's layout) and the 128-token column groups
+// (codes transposed).  The tile and thread layout are those of
+// quant_col_t_kernel; a tile's 128 channels are exactly one row group of each
+// of its 128 tokens (tiles start on multiples of 128), so each token's row
+// maximum reduces over the 8 lanes of a wave that share its token chunk
+// (stride-8 lanes) and then over the two waves that cover the tile's channel
+// halves (LDS).  Both code sets are staged in LDS and stored as whole rows.
+// ---------------------------------------------------------------------------
+// A 128 x 128-byte tile of codes in LDS in the layout of the output (rows of
+// 128 bytes, no padding): the 8-byte chunk c of row r sits in 16-byte slot
+// (c >> 1) ^ ((r >> 3) & 7), half c & 1.  Writers (lane = row chunk r >> 3,
+// 8 rows apart, times chunk) hit 16 distinct slots per 16 lanes; readers take
+// whole 16-byte slots.  Every store instruction then writes 8 full 128-byte
+// rows instead of 64-byte halves of lines from two different waves.
+__device__ __forceinline__ uint32_t row_tile_offset(uint32_t r, uint32_t c) {
+  return r * 128 + ((((c >> 1) ^ ((r >> 3) & 7)) << 4) | ((c & 1) << 3));
+}
+__device__ __forceinline__ void store_row_tile(const uint8_t* rtile, uint8_t* __restrict__ q, int64_t ldq,
+                                               uint32_t r0, uint32_t c0, uint32_t rows, uint32_t cols,
+                                               uint32_t tid) {
+#pragma unroll
+  for (int rep = 0; rep < 4; ++rep) {
+    const uint32_t idx = rep * kThreads + tid;
+    const uint32_t r = idx >> 3, p = idx & 7;
+    if (r0 + r < rows && c0 + p * 16 < cols) {
+      const uint4 v = *reinterpret_cast<const uint4*>(rtile + r * 128 + ((p ^ ((r >> 3) & 7)) << 4));
+      store_nt(q + (int64_t)(r0 + r) * ldq + c0 + p * 16, v);
+    }
+  }
+}
+// The transposed tile of quant_col_t_kernel (rows of kColPitch bytes) out to
+// qt [cols][ldqt]: 16 bytes per lane, 8 lanes per 128-token row.
+__device__ __forceinline__ void store_tile_t(const uint8_t* tile, uint8_t* __restrict__ qt, int64_t ldqt,
+                                             uint32_t c0, uint32_t t0, uint32_t cols, uint32_t rows,
+                                             uint32_t tid) {
+#pragma unroll
+  for (int rep = 0; rep < 4; ++rep) {
+    const uint32_t idx = rep * kThreads + tid;
+    const uint32_t ch = idx >> 3, ck = idx & 7;
+    if (c0 + ch < cols && t0 + ck * 16 < rows) {
+      const uint2 a = *reinterpret_cast<const uint2*>(tile + ch * kColPitch + ck * 16);
+      const uint2 b = *reinterpret_cast<const uint2*>(tile + ch * kColPitch + ck * 16 + 8);
+      store_nt(qt + (int64_t)(c0 + ch) * ldqt + t0 + ck * 16, make_uint4(a.x, a.y, b.x, b.y));
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t max_stride8(uint32_t v) {
+  v = dpp_max<DPP_ROW_ROR8>(v);
+  uint32_t o = (uint32_t)__shfl_xor((int)v, 16);
+  v = v > o ? v : o;
+  o = (uint32_t)__shfl_xor((int)v, 32);
+  return v > o ? v : o;
+}
+
+template <typename InT, int FMT>
+__global__ __launch_bounds__(kThreads) void quant_dual_kernel(
+    const InT* __restrict__ x, uint32_t rows, uint32_t cols, int64_t ldx, uint8_t* __restrict__ q,
+    int64_t ldq, uint8_t* __restrict__ s, uint8_t* __restrict__ qt, int64_t ldqt, uint8_t* __restrict__ st,
+    uint32_t ngc, uint32_t ngt) {
+  __shared__ uint32_t red[2][128];   // column maxima per token half
+  __shared__ uint32_t rred[2][128];  // row maxima per channel half
+  __shared__ int exps[128], rexps[128];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * kColPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t rtile[128 * 128];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint32_t tr = (lane & 7) + 8 * (w & 1);   // token chunk: tokens tr*8 .. tr*8+7
+  const uint32_t tc = (lane >> 3) + 8 * (w >> 1); // channel chunk: channels tc*8 .. tc*8+7
+  const uint32_t c0 = blockIdx.x * 128, t0 = blockIdx.y * 128;
+  const bool cact = c0 + tc * 8 < cols;
+  float f[8][8];  // [token][channel]
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t r = t0 + tr * 8 + i;
+    if (cact && r < rows) load8<false>(x + (int64_t)r * ldx + c0 + tc * 8, f[i]);
+    else zero8(f[i]);
+  }
+  uint32_t m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t a = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = max(a, abs_bits(f[i][j]));
+    m[j] = max_oct(a);
+  }
+  if ((lane & 7) == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[w & 1][tc * 8 + j] = m[j];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t a = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a = max(a, abs_bits(f[i][j]));
+    m[i] = max_stride8(a);
+  }
+  if ((lane >> 3) == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rred[w >> 1][tr * 8 + i] = m[i];
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const uint32_t a = max(red[0][tid], red[1][tid]);
+    const int e = scale_exp_ceil<FMT>(a);
+    exps[tid] = e;
+    if (c0 + tid < cols) st[(int64_t)(c0 + tid) * ngt + blockIdx.y] = (uint8_t)(e + 127);
+  } else {
+    const uint32_t t = tid - 128;
+    const uint32_t a = max(rred[0][t], rred[1][t]);
+    const int e = scale_exp_ceil<FMT>(a);
+    rexps[t] = e;
+    if (t0 + t < rows) s[(int64_t)(t0 + t) * ngc + blockIdx.x] = (uint8_t)(e + 127);
+  }
+  __syncthreads();
+  // Column codes into the transposed tile; row codes into the row tile.
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float sc = pow2_neg(exps[tc * 8 + j]);
+    uint2 o;
+    o.x = cvt4<FMT>(f[0][j] * sc, f[1][j] * sc, f[2][j] * sc, f[3][j] * sc);
+    o.y = cvt4<FMT>(f[4][j] * sc, f[5][j] * sc, f[6][j] * sc, f[7][j] * sc);
+    *reinterpret_cast<uint2*>(tile + (tc * 8 + j) * kColPitch + tr * 8) = o;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint2*>(rtile + row_tile_offset(tr * 8 + i, tc)) =
+        codes8<FMT>(f[i], pow2_neg(rexps[tr * 8 + i]));
+  __syncthreads();
+  store_tile_t(tile, qt, ldqt, c0, t0, cols, rows, tid);
+  store_row_tile(rtile, q, ldq, t0, c0, rows, cols, tid);
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 tiles with both the codes and their transpose (one scale per tile,
+// so the transposed codes are the same bytes): thread layout of
+// quant_col_t_kernel, amax over the whole tile, both code sets staged in LDS
+// (the padded transposed tile and the swizzled row tile).
+// ---------------------------------------------------------------------------
+template <typename InT, int FMT>
+__global__ __launch_bounds__(kThreads) void quant_block_dual_kernel(
+    const InT* __restrict__ w, uint32_t rows, uint32_t cols, int64_t ldw, uint8_t* __restrict__ q,
+    int64_t ldq, uint8_t* __restrict__ s, uint8_t* __restrict__ qt, int64_t ldqt, uint8_t* __restrict__ st,
+    uint32_t nbc, uint32_t nbr) {
+  __shared__ uint32_t red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * kColPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t rtile[128 * 128];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t tr = (lane & 7) + 8 * (wv & 1);   // row chunk: rows tr*8 .. tr*8+7
+  const uint32_t tc = (lane >> 3) + 8 * (wv >> 1); // column chunk: columns tc*8 .. tc*8+7
+  const uint32_t c0 = blockIdx.x * 128, r0 = blockIdx.y * 128;
+  const bool cact = c0 + tc * 8 < cols;
+  float f[8][8];  // [row][column]
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t r = r0 + tr * 8 + i;
+    if (cact && r < rows) load8<false>(w + (int64_t)r * ldw + c0 + tc * 8, f[i]);
+    else zero8(f[i]);
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = max(m, abs_bits(f[i][j]));
+  m = max_wave(m);
+  if (lane == 0) red[wv] = m;
+  __syncthreads();
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  const int e = scale_exp_ceil<FMT>(m);
+  const float sc = pow2_neg(e);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint2 o;
+    o.x = cvt4<FMT>(f[0][j] * sc, f[1][j] * sc, f[2][j] * sc, f[3][j] * sc);
+    o.y = cvt4<FMT>(f[4][j] * sc, f[5][j] * sc, f[6][j] * sc, f[7][j] * sc);
+    *reinterpret_cast<uint2*>(tile + (tc * 8 + j) * kColPitch + tr * 8) = o;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint2*>(rtile + row_tile_offset(tr * 8 + i, tc)) = codes8<FMT>(f[i], sc);
+  if (tid == 0) {
+    s[(int64_t)blockIdx.y * nbc + blockIdx.x] = (uint8_t)(e + 127);
+    st[(int64_t)blockIdx.x * nbr + blockIdx.y] = (uint8_t)(e + 127);
+  }
+  __syncthreads();
+  store_tile_t(tile, qt, ldqt, c0, r0, cols, rows, tid);
+  store_row_tile(rtile, q, ldq, r0, c0, rows, cols, tid);
+}
+
+// ---------------------------------------------------------------------------
 // 128x128 tiles.  One workgroup per tile, the whole tile held in registers
 // (8 rows x 8 columns per thread), amax by DPP + cross-lane shuffles inside
 // each wavefront and 4 values through LDS across wavefronts; then one pass of
@@ -309,6 +499,46 @@ void launch_quant_col_t(const void* x, int dtype, int64_t rows, int64_t cols, in
   } else {
     if (fmt == 0) col_dispatch<float, 0>(x, rows, cols, ldx, qt, ldq, st, stream);
     else col_dispatch<float, 1>(x, rows, cols, ldx, qt, ldq, st, stream);
+  }
+}
+
+template <typename InT, int FMT>
+static void dual_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
+                          uint8_t* s, uint8_t* qt, int64_t ldqt, uint8_t* st, hipStream_t stream) {
+  const uint32_t ngc = (uint32_t)((cols + 127) / 128), ngt = (uint32_t)((rows + 127) / 128);
+  hipLaunchKernelGGL((quant_dual_kernel<InT, FMT>), dim3(ngc, ngt), dim3(kThreads), 0, stream, (const InT*)x,
+                     (uint32_t)rows, (uint32_t)cols, ldx, q, ldq, s, qt, ldqt, st, ngc, ngt);
+}
+
+void launch_quant_dual(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
+                       int64_t ldq, uint8_t* s, uint8_t* qt, int64_t ldqt, uint8_t* st, hipStream_t stream) {
+  if (dtype == 1) {
+    if (fmt == 0) dual_dispatch<uint16_t, 0>(x, rows, cols, ldx, q, ldq, s, qt, ldqt, st, stream);
+    else dual_dispatch<uint16_t, 1>(x, rows, cols, ldx, q, ldq, s, qt, ldqt, st, stream);
+  } else {
+    if (fmt == 0) dual_dispatch<float, 0>(x, rows, cols, ldx, q, ldq, s, qt, ldqt, st, stream);
+    else dual_dispatch<float, 1>(x, rows, cols, ldx, q, ldq, s, qt, ldqt, st, stream);
+  }
+}
+
+template <typename InT, int FMT>
+static void block_dual_dispatch(const void* w, int64_t rows, int64_t cols, int64_t ldw, uint8_t* q,
+                                int64_t ldq, uint8_t* s, uint8_t* qt, int64_t ldqt, uint8_t* st,
+                                hipStream_t stream) {
+  const uint32_t nbc = (uint32_t)((cols + 127) / 128), nbr = (uint32_t)((rows + 127) / 128);
+  hipLaunchKernelGGL((quant_block_dual_kernel<InT, FMT>), dim3(nbc, nbr), dim3(kThreads), 0, stream,
+                     (const InT*)w, (uint32_t)rows, (uint32_t)cols, ldw, q, ldq, s, qt, ldqt, st, nbc, nbr);
+}
+
+void launch_quant_block_dual(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw, int fmt,
+                             uint8_t* q, int64_t ldq, uint8_t* s, uint8_t* qt, int64_t ldqt, uint8_t* st,
+                             hipStream_t stream) {
+  if (dtype == 1) {
+    if (fmt == 0) block_dual_dispatch<uint16_t, 0>(w, rows, cols, ldw, q, ldq, s, qt, ldqt, st, stream);
+    else block_dual_dispatch<uint16_t, 1>(w, rows, cols, ldw, q, ldq, s, qt, ldqt, st, stream);
+  } else {
+    if (fmt == 0) block_dual_dispatch<float, 0>(w, rows, cols, ldw, q, ldq, s, qt, ldqt, st, stream);
+    else block_dual_dispatch<float, 1>(w, rows, cols, ldw, q, ldq, s, qt, ldqt, st, stream);
   }
 }
 

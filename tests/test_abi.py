@@ -26,7 +26,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = mx.load_library()
     names = declared_functions()
     assert set(names) >= {"fp8_quantize_token", "fp8_quantize_block", "mx_quantize", "fp8_block_scaled_gemm",
-                          "mx_gemm", "mxfp8_status_string", "mxfp8_version"}
+                          "mx_gemm", "fp8_quantize_token_dual", "fp8_quantize_block_dual",
+                          "mxfp8_status_string", "mxfp8_version"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -71,6 +72,26 @@ def test_block_validation():
     assert blk(ldw=16) == LD and blk(ldq=520) == LD
     assert blk(w=MIS) == ALIGN
     assert blk(q=X) == ALIAS
+
+
+Q2, S2 = 0x600000, 0x700000
+
+
+@pytest.mark.parametrize("fn", ["fp8_quantize_token_dual", "fp8_quantize_block_dual"])
+def test_dual_validation(fn):
+    f = getattr(mx, fn)
+
+    def call(x=X, dt=1, rows=256, cols=512, ldx=512, fmt=0, q=Q, ldq=512, s=S, qt=Q2, ldqt=256, st=S2):
+        return f(x, dt, rows, cols, ldx, fmt, q, ldq, s, qt, ldqt, st, None)
+    assert call(fmt=2) == ENUM and call(dt=3) == ENUM
+    assert call(rows=-16) == SHAPE and call(rows=2 ** 31) == SHAPE
+    assert call(rows=0, x=None, q=None, qt=None) == OK and call(cols=0, s=None, st=None) == OK
+    assert call(rows=136, ldqt=144) == SHAPE and call(cols=520, ldx=528, ldq=528) == SHAPE
+    assert call(x=None) == NULL and call(q=None) == NULL and call(qt=None) == NULL and call(st=None) == NULL
+    assert call(ldx=500) == LD and call(ldq=500) == LD and call(ldqt=240) == LD and call(ldqt=264) == LD
+    assert call(x=MIS) == ALIGN and call(qt=MIS) == ALIGN
+    assert call(q=X) == ALIAS and call(qt=X) == ALIAS and call(st=X) == ALIAS
+    assert call(qt=Q) == ALIAS and call(st=Q) == ALIAS and call(qt=S) == ALIAS and call(st=S) == ALIAS
 
 
 def mxq(x=X, dt=0, rows=64, cols=256, ldx=256, fmt=0, rule=1, q=Q, ldq=256, s=S, cnt=P2):
