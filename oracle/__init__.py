@@ -62,6 +62,15 @@ def _load():
         for name in ("orc_quantize_rows", "orc_quantize_cols_t", "orc_quantize_block"):
             getattr(lib, name).argtypes = [P, I, I64, I64, I64, I, P, I64, P]
             getattr(lib, name).restype = None
+        lib.orc_scale_f32.argtypes = [I, ctypes.c_float]
+        lib.orc_scale_f32.restype = ctypes.c_float
+        for name in ("orc_quantize_rows_f32s", "orc_quantize_cols_t_f32s", "orc_quantize_block_f32s"):
+            getattr(lib, name).argtypes = [P, I, I64, I64, I64, I, P, I64, P]
+            getattr(lib, name).restype = None
+        lib.orc_gemm_f32s.argtypes = [I64, I64, I64, P, I64, I, P, P, I64, I, I, P, I, I64, I64, P, P, I64]
+        lib.orc_gemm_f32s.restype = None
+        lib.orc_gemm_f32s_elems.argtypes = [I64, I64, I64, P, I64, I, P, P, I64, I, I, P, I, P, P, I64, P, P]
+        lib.orc_gemm_f32s_elems.restype = None
         lib.orc_mx_quantize.argtypes = [P, I, I64, I64, I64, I, I, P, I64, P, P]
         lib.orc_mx_quantize.restype = None
         lib.orc_gemm.argtypes = [I64, I64, I64, P, I64, I, P, P, I64, I, I, P, I,
@@ -209,6 +218,66 @@ def quantize_block(w, fmt, threads=1):
     return q, s
 
 
+def scale_f32(fmt, amax):
+    """The fp32 scale amax / fmax of a group (1 when amax == 0)."""
+    return np.float32(_load().orc_scale_f32(fmt, float(np.float32(amax))))
+
+
+def quantize_rows_f32s(x, fmt, threads=1):
+    """1x128 groups along rows with fp32 scales: (q u8, s float32 [rows][ceil(cols/128)])."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    dt, es = _dtype_code(x)
+    rows, cols = x.shape
+    ng = -(-cols // 128)
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows, ng), np.float32)
+
+    def job(r0, r1):
+        return lambda: lib.orc_quantize_rows_f32s(
+            ctypes.c_void_p(x.ctypes.data + r0 * cols * es), dt, r1 - r0, cols, cols, fmt,
+            ctypes.c_void_p(q.ctypes.data + r0 * cols), cols, ctypes.c_void_p(s.ctypes.data + 4 * r0 * ng))
+    _run([job(a, b) for a, b in _split(rows, threads)])
+    return q, s
+
+
+def quantize_cols_t_f32s(x, fmt, threads=1):
+    """128-token groups down columns, transposed, fp32 scales: (qt u8 [cols][rows], st float32)."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    dt, es = _dtype_code(x)
+    rows, cols = x.shape
+    ng = -(-rows // 128)
+    qt = np.empty((cols, rows), np.uint8)
+    st = np.empty((cols, ng), np.float32)
+
+    def job(c0, c1):
+        return lambda: lib.orc_quantize_cols_t_f32s(
+            ctypes.c_void_p(x.ctypes.data + c0 * es), dt, rows, c1 - c0, cols, fmt,
+            ctypes.c_void_p(qt.ctypes.data + c0 * rows), rows, ctypes.c_void_p(st.ctypes.data + 4 * c0 * ng))
+    _run([job(a, b) for a, b in _split(cols, threads)])
+    return qt, st
+
+
+def quantize_block_f32s(w, fmt, threads=1):
+    """128x128 tiles with fp32 scales: (q u8, s float32 [ceil(rows/128)][ceil(cols/128)])."""
+    lib = _load()
+    w = np.ascontiguousarray(w)
+    dt, es = _dtype_code(w)
+    rows, cols = w.shape
+    nbr, nbc = -(-rows // 128), -(-cols // 128)
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((nbr, nbc), np.float32)
+
+    def job(i0, i1):
+        r0, r1 = i0 * 128, min(i1 * 128, rows)
+        return lambda: lib.orc_quantize_block_f32s(
+            ctypes.c_void_p(w.ctypes.data + r0 * cols * es), dt, r1 - r0, cols, cols, fmt,
+            ctypes.c_void_p(q.ctypes.data + r0 * cols), cols, ctypes.c_void_p(s.ctypes.data + 4 * i0 * nbc))
+    _run([job(a, b) for a, b in _split(nbr, threads)])
+    return q, s
+
+
 def mx_quantize(x, fmt, rule=RULE_FLOOR, threads=1):
     """32-element blocks along rows: returns (q, s, counts) with s, counts [rows][ceil(cols/32)]."""
     lib = _load()
@@ -321,6 +390,56 @@ def mx_gemm_elems(a, sa, a_fmt, b, sb, b_fmt, ii, jj, threads=1):
     def job(i0, i1):
         return lambda: lib.orc_mx_gemm_elems(
             M, N, K, _ptr(a), K, a_fmt, _ptr(sa), _ptr(b), K, b_fmt, _ptr(sb),
+            ctypes.c_void_p(ii.ctypes.data + 8 * i0), ctypes.c_void_p(jj.ctypes.data + 8 * i0), i1 - i0,
+            ctypes.c_void_p(y.ctypes.data + 8 * i0), ctypes.c_void_p(t.ctypes.data + 8 * i0))
+    _run([job(i0, i1) for i0, i1 in _split(n, threads)])
+    return y, t
+
+
+def _f32s_operands(a, sa, b, sb, b_layout):
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    if np.asarray(sa).dtype != np.float32 or np.asarray(sb).dtype != np.float32:
+        raise TypeError("fp32-scale GEMM: scales must be float32 arrays")
+    sa = np.ascontiguousarray(sa)
+    sb = np.ascontiguousarray(sb)
+    M, K = a.shape
+    N = b.shape[0] if b_layout == B_NK else b.shape[1]
+    if (b.shape[1] if b_layout == B_NK else b.shape[0]) != K:
+        raise ValueError("A and B disagree on K")
+    return a, sa, b, sb, M, N, K
+
+
+def gemm_f32s(a, sa, a_fmt, b, sb, b_fmt, b_layout=B_NK, b_scale=B_SCALE_BLOCK, threads=1):
+    """GEMM over operands with fp32 scales (layouts of gemm, float32 instead of bytes):
+    y = sum_k a(m,k) b(k,n), t = sum_k |a b|, fp64 [M][N]."""
+    lib = _load()
+    a, sa, b, sb, M, N, K = _f32s_operands(a, sa, b, sb, b_layout)
+    y = np.empty((M, N), np.float64)
+    t = np.empty((M, N), np.float64)
+    ldb = b.shape[1]
+
+    def job(m0, m1):
+        return lambda: lib.orc_gemm_f32s(M, N, K, _ptr(a), K, a_fmt, _ptr(sa), _ptr(b), ldb, b_fmt, b_layout,
+                                         _ptr(sb), b_scale, m0, m1, _ptr(y), _ptr(t), N)
+    _run([job(m0, m1) for m0, m1 in _split(M, threads)])
+    return y, t
+
+
+def gemm_f32s_elems(a, sa, a_fmt, b, sb, b_fmt, ii, jj, b_layout=B_NK, b_scale=B_SCALE_BLOCK, threads=1):
+    """gemm_f32s for the listed output elements (ii[i], jj[i])."""
+    lib = _load()
+    a, sa, b, sb, M, N, K = _f32s_operands(a, sa, b, sb, b_layout)
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    n = ii.size
+    y = np.empty(n, np.float64)
+    t = np.empty(n, np.float64)
+    ldb = b.shape[1]
+
+    def job(i0, i1):
+        return lambda: lib.orc_gemm_f32s_elems(
+            M, N, K, _ptr(a), K, a_fmt, _ptr(sa), _ptr(b), ldb, b_fmt, b_layout, _ptr(sb), b_scale,
             ctypes.c_void_p(ii.ctypes.data + 8 * i0), ctypes.c_void_p(jj.ctypes.data + 8 * i0), i1 - i0,
             ctypes.c_void_p(y.ctypes.data + 8 * i0), ctypes.c_void_p(t.ctypes.data + 8 * i0))
     _run([job(i0, i1) for i0, i1 in _split(n, threads)])

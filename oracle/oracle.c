@@ -52,6 +52,12 @@
  *   R7  the GEMM result is the exact sum over k of the dequantized products;
  *       here it is accumulated in fp64 (sequential over k), together with
  *       sum_k |a*b| which sizes the tolerance.
+ *   R8  "FP8 with an FP32 scale" (named on the recipe page's review as a
+ *       variant of its Table 4, not defined there): the scale is not rounded
+ *       to a power of two but is the fp32 quotient s = amax / fmax (IEEE
+ *       single precision, round to nearest even; s = 1 when amax == 0), and
+ *       each code is the saturating cast of the fp32 quotient x / s.  Both
+ *       divisions are IEEE fp32 operations, so the codes are fixed bits.
  */
 #include "oracle.h"
 
@@ -283,6 +289,80 @@ void orc_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64
 }
 
 /* ---------------------------------------------------------------------- */
+/* Quantizers with fp32 scales (R8)                                         */
+/* ---------------------------------------------------------------------- */
+
+/* The fp32 scale of a group whose largest magnitude is amax (an fp32 value:
+ * the inputs are fp32 or bf16): amax / fmax in IEEE single precision. */
+float orc_scale_f32(int fmt, float amax) {
+  if (amax == 0.0f) return 1.0f;
+  const float fmax = (float)fmax_of(fmt);
+  return amax / fmax;
+}
+
+/* Code of one element under an fp32 scale: the fp32 quotient x / s, then
+ * the saturating cast (R3). */
+static uint8_t encode_div(int fmt, double x, float s) {
+  const float v = (float)x / s; /* x is an fp32 (or bf16) value: exact */
+  return orc_encode(fmt, (double)v);
+}
+
+/* Largest magnitude of the elements r0..r1-1 x c0..c1-1, as fp32. */
+static float group_amax(const void* x, int dtype, int64_t ldx, int64_t r0, int64_t r1, int64_t c0,
+                        int64_t c1) {
+  double amax = 0.0;
+  for (int64_t r = r0; r < r1; ++r)
+    for (int64_t c = c0; c < c1; ++c) {
+      const double a = fabs(load_elem(x, dtype, r * ldx + c));
+      if (a > amax) amax = a;
+    }
+  return (float)amax; /* exact: amax is one of the fp32 inputs */
+}
+
+/* Token-wise 1x128 groups along rows with fp32 scales (R8);
+ * s[r*ceil(cols/128) + g] = the group's fp32 scale. */
+void orc_quantize_rows_f32s(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                            int fmt, uint8_t* q, int64_t ldq, float* s) {
+  const int64_t G = 128, ng = ceil_div(cols, G);
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t g = 0; g < ng; ++g) {
+      const int64_t c0 = g * G, c1 = min64(c0 + G, cols);
+      const float sc = orc_scale_f32(fmt, group_amax(x, dtype, ldx, r, r + 1, c0, c1));
+      s[r * ng + g] = sc;
+      for (int64_t c = c0; c < c1; ++c) q[r * ldq + c] = encode_div(fmt, load_elem(x, dtype, r * ldx + c), sc);
+    }
+}
+
+/* 128-token groups down columns, written transposed, with fp32 scales (R8):
+ * qt[c*ldq + r], st[c*ceil(rows/128) + t]. */
+void orc_quantize_cols_t_f32s(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                              int fmt, uint8_t* qt, int64_t ldq, float* st) {
+  const int64_t G = 128, ng = ceil_div(rows, G);
+  for (int64_t c = 0; c < cols; ++c)
+    for (int64_t t = 0; t < ng; ++t) {
+      const int64_t r0 = t * G, r1 = min64(r0 + G, rows);
+      const float sc = orc_scale_f32(fmt, group_amax(x, dtype, ldx, r0, r1, c, c + 1));
+      st[c * ng + t] = sc;
+      for (int64_t r = r0; r < r1; ++r) qt[c * ldq + r] = encode_div(fmt, load_elem(x, dtype, r * ldx + c), sc);
+    }
+}
+
+/* 128x128 tiles with fp32 scales (R8): s[i*ceil(cols/128) + j]. */
+void orc_quantize_block_f32s(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw,
+                             int fmt, uint8_t* q, int64_t ldq, float* s) {
+  const int64_t G = 128, nbr = ceil_div(rows, G), nbc = ceil_div(cols, G);
+  for (int64_t i = 0; i < nbr; ++i)
+    for (int64_t j = 0; j < nbc; ++j) {
+      const int64_t r0 = i * G, r1 = min64(r0 + G, rows);
+      const int64_t c0 = j * G, c1 = min64(c0 + G, cols);
+      const float sc = orc_scale_f32(fmt, group_amax(w, dtype, ldw, r0, r1, c0, c1));
+      s[i * nbc + j] = sc;
+      for (int64_t r = r0; r < r1; ++r)
+        for (int64_t c = c0; c < c1; ++c) q[r * ldq + c] = encode_div(fmt, load_elem(w, dtype, r * ldw + c), sc);
+    }
+}
+
+/* ---------------------------------------------------------------------- */
 /* Block-scaled GEMM [INFR "What carries the argument"; R7]                */
 /* ---------------------------------------------------------------------- */
 
@@ -356,6 +436,76 @@ void orc_gemm_elems(int64_t M, int64_t N, int64_t K,
     for (int64_t k = 0; k < K; ++k) {
       const double p = a_value(K, a, lda, a_fmt, sa, ii[i], k) *
                        b_value(N, K, b, ldb, b_fmt, b_layout, sb, b_scale, k, jj[i]);
+      acc += p;
+      mag += fabs(p);
+    }
+    y[i] = acc;
+    t[i] = mag;
+  }
+}
+
+/* GEMM over operands with fp32 scales (R8, R7): a(m,k) = dec(A[m][k]) *
+ * sa[m][k/128], b(k,n) = dec(B(k,n)) * sb(k/128, n) with the scale layouts of
+ * orc_gemm (floats instead of bytes).  Each dequantized element is exact in
+ * fp64 (a 4-bit significand times a 24-bit one). */
+static double a_value_f32s(int64_t K, const uint8_t* a, int64_t lda, int a_fmt, const float* sa, int64_t m,
+                           int64_t k) {
+  const int64_t nkb = ceil_div(K, 128);
+  return orc_decode(a_fmt, a[m * lda + k]) * (double)sa[m * nkb + k / 128];
+}
+
+static double b_value_f32s(int64_t N, int64_t K, const uint8_t* b, int64_t ldb, int b_fmt, int b_layout,
+                           const float* sb, int b_scale, int64_t k, int64_t n) {
+  const int64_t nkb = ceil_div(K, 128), nnb = ceil_div(N, 128);
+  const uint8_t code = b_layout == 0 ? b[n * ldb + k] : b[k * ldb + n];
+  double scale;
+  if (b_scale == 1) scale = sb[n * nkb + k / 128];
+  else if (b_layout == 0) scale = sb[(n / 128) * nkb + k / 128];
+  else scale = sb[(k / 128) * nnb + n / 128];
+  return orc_decode(b_fmt, code) * scale;
+}
+
+void orc_gemm_f32s(int64_t M, int64_t N, int64_t K,
+                   const uint8_t* a, int64_t lda, int a_fmt, const float* sa,
+                   const uint8_t* b, int64_t ldb, int b_fmt, int b_layout,
+                   const float* sb, int b_scale,
+                   int64_t m0, int64_t m1, double* y, double* t, int64_t ldy) {
+  (void)M;
+  double* bd = (double*)malloc(sizeof(double) * (size_t)(N * K > 0 ? N * K : 1));
+  double* ad = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+  if (!bd || !ad) { free(bd); free(ad); abort(); }
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k)
+      bd[n * K + k] = b_value_f32s(N, K, b, ldb, b_fmt, b_layout, sb, b_scale, k, n);
+  for (int64_t m = m0; m < m1; ++m) {
+    for (int64_t k = 0; k < K; ++k) ad[k] = a_value_f32s(K, a, lda, a_fmt, sa, m, k);
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0, mag = 0.0;
+      const double* bn = bd + n * K;
+      for (int64_t k = 0; k < K; ++k) {
+        const double p = ad[k] * bn[k];
+        acc += p;
+        mag += fabs(p);
+      }
+      y[m * ldy + n] = acc;
+      t[m * ldy + n] = mag;
+    }
+  }
+  free(ad);
+  free(bd);
+}
+
+void orc_gemm_f32s_elems(int64_t M, int64_t N, int64_t K,
+                         const uint8_t* a, int64_t lda, int a_fmt, const float* sa,
+                         const uint8_t* b, int64_t ldb, int b_fmt, int b_layout,
+                         const float* sb, int b_scale,
+                         const int64_t* ii, const int64_t* jj, int64_t n, double* y, double* t) {
+  (void)M;
+  for (int64_t i = 0; i < n; ++i) {
+    double acc = 0.0, mag = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double p = a_value_f32s(K, a, lda, a_fmt, sa, ii[i], k) *
+                       b_value_f32s(N, K, b, ldb, b_fmt, b_layout, sb, b_scale, k, jj[i]);
       acc += p;
       mag += fabs(p);
     }

@@ -40,6 +40,14 @@ void orc_quantize_block(const void* w, int dtype, int64_t rows, int64_t cols, in
 void orc_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                      int fmt, int rule, uint8_t* q, int64_t ldq, uint8_t* s, uint8_t* counts);
 
+float orc_scale_f32(int fmt, float amax);
+void orc_quantize_rows_f32s(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                            int fmt, uint8_t* q, int64_t ldq, float* s);
+void orc_quantize_cols_t_f32s(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                              int fmt, uint8_t* qt, int64_t ldq, float* st);
+void orc_quantize_block_f32s(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw,
+                             int fmt, uint8_t* q, int64_t ldq, float* s);
+
 void orc_gemm(int64_t M, int64_t N, int64_t K,
               const uint8_t* a, int64_t lda, int a_fmt, const uint8_t* sa,
               const uint8_t* b, int64_t ldb, int b_fmt, int b_layout,
@@ -50,6 +58,17 @@ void orc_gemm_elems(int64_t M, int64_t N, int64_t K,
                     const uint8_t* b, int64_t ldb, int b_fmt, int b_layout,
                     const uint8_t* sb, int b_scale,
                     const int64_t* ii, const int64_t* jj, int64_t n, double* y, double* t);
+
+void orc_gemm_f32s(int64_t M, int64_t N, int64_t K,
+                   const uint8_t* a, int64_t lda, int a_fmt, const float* sa,
+                   const uint8_t* b, int64_t ldb, int b_fmt, int b_layout,
+                   const float* sb, int b_scale,
+                   int64_t m0, int64_t m1, double* y, double* t, int64_t ldy);
+void orc_gemm_f32s_elems(int64_t M, int64_t N, int64_t K,
+                         const uint8_t* a, int64_t lda, int a_fmt, const float* sa,
+                         const uint8_t* b, int64_t ldb, int b_fmt, int b_layout,
+                         const float* sb, int b_scale,
+                         const int64_t* ii, const int64_t* jj, int64_t n, double* y, double* t);
 
 void orc_mx_gemm(int64_t M, int64_t N, int64_t K,
                  const uint8_t* a, int64_t lda, int a_fmt, const uint8_t* sa,
