@@ -55,8 +55,9 @@
  *   R8  "FP8 with an FP32 scale" (named on the recipe page's review as a
  *       variant of its Table 4, not defined there): the scale is not rounded
  *       to a power of two but is the fp32 quotient s = amax / fmax (IEEE
- *       single precision, round to nearest even; s = 1 when amax == 0), and
- *       each code is the saturating cast of the fp32 quotient x / s.  Both
+ *       single precision, round to nearest even; s = 1 when that quotient
+ *       is zero, i.e. amax == 0 or amax < fmax * 2^-150), and each code is
+ *       the saturating cast of the fp32 quotient x / s.  Both
  *       divisions are IEEE fp32 operations, so the codes are fixed bits.
  */
 #include "oracle.h"
@@ -293,11 +294,13 @@ void orc_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64
 /* ---------------------------------------------------------------------- */
 
 /* The fp32 scale of a group whose largest magnitude is amax (an fp32 value:
- * the inputs are fp32 or bf16): amax / fmax in IEEE single precision. */
+ * the inputs are fp32 or bf16): amax / fmax in IEEE single precision; a
+ * quotient that rounds to zero (amax == 0, or amax below fmax * 2^-150) is
+ * replaced by 1, so that every quotient x / s below is finite. */
 float orc_scale_f32(int fmt, float amax) {
-  if (amax == 0.0f) return 1.0f;
   const float fmax = (float)fmax_of(fmt);
-  return amax / fmax;
+  const float s = amax / fmax;
+  return s == 0.0f ? 1.0f : s;
 }
 
 /* Code of one element under an fp32 scale: the fp32 quotient x / s, then

@@ -1,7 +1,8 @@
 """Pins for the oracle's fp32-scale variant ("FP8 with an FP32 scale", named on
 the review page of "A Comprehensive FP8 Training Recipe for Reasoning-Enhanced
 Language Models" as a Table 4 variant; read here as: scale = amax / fmax in
-IEEE fp32, code = saturating cast of the fp32 quotient x / scale).
+IEEE fp32, 1 where that quotient is zero, code = saturating cast of the fp32
+quotient x / scale).
 
 Independent checks: numpy's own float32 division for the scale and the
 quotient, the nearest-code search over torch's decode table for the cast, the
@@ -28,7 +29,8 @@ def f32_values(x):
 def bf_quantize(vals_f32, fmt):
     """One group: numpy float32 scale and quotient, then the nearest-code search."""
     amax = np.max(np.abs(vals_f32)) if vals_f32.size else np.float32(0)
-    s = np.float32(1.0) if amax == 0 else np.float32(amax) / np.float32(FMAX[fmt])
+    s = np.float32(amax) / np.float32(FMAX[fmt])
+    s = np.float32(1.0) if s == 0 else s
     with np.errstate(over="ignore", divide="ignore"):
         v = vals_f32 / s
     return nearest_code_encoder(v.astype(np.float64), TDT[fmt], FMAX[fmt]), s
@@ -38,10 +40,13 @@ def bf_quantize(vals_f32, fmt):
 def test_scale_is_ieee_single_division(fmt):
     rng = np.random.default_rng(3)
     bits = rng.integers(1, 0x7F7FFFFF, 20000, dtype=np.uint32)
-    amaxes = np.concatenate([bits.view(np.float32), np.float32([1e-45, 1e-40, 448.0, 57344.0, 3.4e38])])
+    amaxes = np.concatenate([bits.view(np.float32), np.float32([1e-40, 2e-43, 448.0, 57344.0, 3.4e38])])
     for a in amaxes:
-        assert oracle.scale_f32(fmt, a) == np.float32(a) / np.float32(FMAX[fmt]), a
+        q = np.float32(a) / np.float32(FMAX[fmt])
+        assert oracle.scale_f32(fmt, a) == (q if q != 0 else np.float32(1.0)), a
+    # a quotient that rounds to zero is replaced by 1, like an all-zero group
     assert oracle.scale_f32(fmt, 0.0) == 1.0
+    assert oracle.scale_f32(fmt, 1e-45) == 1.0 and np.float32(1e-45) / np.float32(FMAX[fmt]) == 0
 
 
 @pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
@@ -55,6 +60,27 @@ def test_rows_vs_bruteforce(fmt, bf16):
             qr, sr = bf_quantize(xf[r, c0:c0 + 128], fmt)
             assert s[r, g] == sr
             assert np.array_equal(q[r, c0:c0 + 128], qr)
+
+
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+def test_tiny_and_subnormal_groups(fmt):
+    """Groups of fp32 subnormals: scales that are themselves subnormal (few
+    significant bits, quotients above fmax that saturate) and scales whose
+    quotient underflows (replaced by 1)."""
+    rng = np.random.default_rng(36)
+    x = np.zeros((4, 256), np.float32)
+    x[0, :128] = (rng.standard_normal(128) * 1e-39).astype(np.float32)
+    x[1, :128] = (rng.integers(-5, 6, 128) * 1e-45).astype(np.float32)
+    x[2, :128] = -0.0
+    x[3, :128] = (rng.standard_normal(128) * 1e-41).astype(np.float32)
+    x[:, 128:] = (rng.standard_normal((4, 128)) * 1e-44).astype(np.float32)
+    q, s = oracle.quantize_rows_f32s(x, fmt)
+    for r in range(4):
+        for g in range(2):
+            qr, sr = bf_quantize(x[r, 128 * g:128 * (g + 1)], fmt)
+            assert s[r, g] == sr
+            assert np.array_equal(q[r, 128 * g:128 * (g + 1)], qr)
+    assert np.all(q[2, :128] == 0x80)
 
 
 @pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
