@@ -114,6 +114,27 @@ int fp8_quantize_block(const void* w, int w_dtype, int64_t rows, int64_t cols, i
                        int fmt, uint8_t* q, int64_t ldq, uint8_t* scales, void* stream);
 
 /*
+ * fp8_quantize_token_f32s, fp8_quantize_block_f32s -- the token-wise and the
+ * block-wise quantizers with fp32 scales instead of power-of-two bytes: the
+ * "FP8 w. FP32 scale" variant that the recipe's Table 4 compares [INFR, review
+ * page, the referee's minor comment on Section 5.2.1, which names it; the page
+ * does not define it, so it is read here as ordinary fp32 scaling]:
+ *   s    = amax / fmax in IEEE fp32 (round to nearest even); s = 1 where
+ *          that quotient is zero (amax == 0, or amax < fmax * 2^-150);
+ *   code = cast(x / s), the fp32 quotient cast with round-to-nearest-even,
+ *          saturating at +-fmax (the rounding of s can put a quotient a
+ *          little above fmax).
+ * Arguments, groups, layouts and requirements are those of
+ * fp8_quantize_token and fp8_quantize_block, with `scales` an array of fp32
+ * (4-byte aligned, MXFP8_ERR_ALIGN otherwise) in the same layout.  A value is
+ * recovered as dec(code) * s.
+ */
+int fp8_quantize_token_f32s(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                            int axis, int fmt, uint8_t* q, int64_t ldq, float* scales, void* stream);
+int fp8_quantize_block_f32s(const void* w, int w_dtype, int64_t rows, int64_t cols, int64_t ldw,
+                            int fmt, uint8_t* q, int64_t ldq, float* scales, void* stream);
+
+/*
  * fp8_quantize_token_dual -- both orientations of fp8_quantize_token from one
  * read of x: the ROW groups that the forward GEMM consumes and the transposed
  * COL_T groups that the weight-gradient GEMM consumes [INFR "What carries the
@@ -198,6 +219,29 @@ int fp8_block_scaled_gemm(int64_t M, int64_t N, int64_t K,
                           const uint8_t* b, int64_t ldb, int b_fmt, int b_layout,
                           const uint8_t* b_scales, int b_scale_mode,
                           void* c, int64_t ldc, int c_dtype, void* stream);
+
+/*
+ * fp8_gemm_f32s -- fp8_block_scaled_gemm over operands with fp32 scales (the
+ * output of fp8_quantize_token_f32s / fp8_quantize_block_f32s; the "FP8 w.
+ * FP32 scale" variant, see those):
+ *
+ *   C[m][n] = sum over 128-wide K blocks kb of
+ *             sa(m,kb) * sb(kb,n) * sum_{k in kb} dec(A[m][k]) * dec(B(k, n)).
+ *
+ * Arguments, layouts and requirements are those of fp8_block_scaled_gemm,
+ * with a_scales and b_scales arrays of fp32 (4-byte aligned) in the same
+ * layouts.  Each K block's product is accumulated by the matrix cores in
+ * fp32 (with the alignment described for fp8_block_scaled_gemm) and added
+ * into the fp32 result times fl(sa * sb) with one fused multiply-add (per-
+ * column B scales: times fl(sa * sb(n))); the scale product's rounding adds at
+ * most 2^-23 * sum_k |a_mk * b_kn| to the bound of fp8_block_scaled_gemm.
+ * Runs on 128x128 tiles.
+ */
+int fp8_gemm_f32s(int64_t M, int64_t N, int64_t K,
+                  const uint8_t* a, int64_t lda, int a_fmt, const float* a_scales,
+                  const uint8_t* b, int64_t ldb, int b_fmt, int b_layout,
+                  const float* b_scales, int b_scale_mode,
+                  void* c, int64_t ldc, int c_dtype, void* stream);
 
 /*
  * mx_gemm -- C = A * B over MX operands: FP8 elements with one E8M0 scale

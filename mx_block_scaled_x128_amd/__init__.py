@@ -8,11 +8,13 @@ entry point raises -- there is no fallback path.
 
 Low-level entry points carry the C names and signatures (pointers as ints):
   fp8_quantize_token, fp8_quantize_block, fp8_quantize_token_dual,
-  fp8_quantize_block_dual, mx_quantize, fp8_block_scaled_gemm, mx_gemm,
+  fp8_quantize_block_dual, fp8_quantize_token_f32s, fp8_quantize_block_f32s,
+  mx_quantize, fp8_block_scaled_gemm, fp8_gemm_f32s, mx_gemm,
   mxfp8_status_string, mxfp8_version.
 Tensor conveniences allocate outputs with torch and call them:
   quantize_token, quantize_block, quantize_token_dual, quantize_block_dual,
-  quantize_mx, block_scaled_gemm, mx_scaled_gemm.
+  quantize_token_f32s, quantize_block_f32s, quantize_mx, block_scaled_gemm,
+  gemm_f32s, mx_scaled_gemm.
 """
 import ctypes
 import os
@@ -22,9 +24,11 @@ __all__ = [
     "E4M3", "E5M2", "F32", "BF16", "ROW", "COL_T", "RULE_CEIL", "RULE_FLOOR", "B_NK", "B_KN",
     "SCALE_BLOCK128", "SCALE_ROW128", "MxFp8Error", "library_path", "load_library",
     "fp8_quantize_token", "fp8_quantize_block", "fp8_quantize_token_dual", "fp8_quantize_block_dual",
-    "mx_quantize", "fp8_block_scaled_gemm", "mx_gemm", "mxfp8_status_string", "mxfp8_version",
-    "quantize_token", "quantize_block", "quantize_token_dual", "quantize_block_dual", "quantize_mx",
-    "block_scaled_gemm", "mx_scaled_gemm",
+    "fp8_quantize_token_f32s", "fp8_quantize_block_f32s", "mx_quantize", "fp8_block_scaled_gemm",
+    "fp8_gemm_f32s", "mx_gemm", "mxfp8_status_string", "mxfp8_version",
+    "quantize_token", "quantize_block", "quantize_token_dual", "quantize_block_dual",
+    "quantize_token_f32s", "quantize_block_f32s", "quantize_mx", "block_scaled_gemm", "gemm_f32s",
+    "mx_scaled_gemm",
 ]
 
 # enum values of include/mxfp8.h
@@ -70,10 +74,16 @@ def load_library():
         lib.fp8_quantize_token_dual.restype = I
         lib.fp8_quantize_block_dual.argtypes = [P, I, I64, I64, I64, I, P, I64, P, P, I64, P, P]
         lib.fp8_quantize_block_dual.restype = I
+        lib.fp8_quantize_token_f32s.argtypes = [P, I, I64, I64, I64, I, I, P, I64, P, P]
+        lib.fp8_quantize_token_f32s.restype = I
+        lib.fp8_quantize_block_f32s.argtypes = [P, I, I64, I64, I64, I, P, I64, P, P]
+        lib.fp8_quantize_block_f32s.restype = I
         lib.mx_quantize.argtypes = [P, I, I64, I64, I64, I, I, P, I64, P, P, P]
         lib.mx_quantize.restype = I
         lib.fp8_block_scaled_gemm.argtypes = [I64, I64, I64, P, I64, I, P, P, I64, I, I, P, I, P, I64, I, P]
         lib.fp8_block_scaled_gemm.restype = I
+        lib.fp8_gemm_f32s.argtypes = [I64, I64, I64, P, I64, I, P, P, I64, I, I, P, I, P, I64, I, P]
+        lib.fp8_gemm_f32s.restype = I
         lib.mx_gemm.argtypes = [I64, I64, I64, P, I64, I, P, P, I64, I, P, P, I64, I, P]
         lib.mx_gemm.restype = I
         lib.mxfp8_status_string.argtypes = [I]
@@ -92,6 +102,14 @@ def fp8_quantize_token(x, x_dtype, rows, cols, ldx, axis, fmt, q, ldq, scales, s
 
 def fp8_quantize_block(w, w_dtype, rows, cols, ldw, fmt, q, ldq, scales, stream):
     return load_library().fp8_quantize_block(w, w_dtype, rows, cols, ldw, fmt, q, ldq, scales, stream)
+
+
+def fp8_quantize_token_f32s(x, x_dtype, rows, cols, ldx, axis, fmt, q, ldq, scales, stream):
+    return load_library().fp8_quantize_token_f32s(x, x_dtype, rows, cols, ldx, axis, fmt, q, ldq, scales, stream)
+
+
+def fp8_quantize_block_f32s(w, w_dtype, rows, cols, ldw, fmt, q, ldq, scales, stream):
+    return load_library().fp8_quantize_block_f32s(w, w_dtype, rows, cols, ldw, fmt, q, ldq, scales, stream)
 
 
 def fp8_quantize_token_dual(x, x_dtype, rows, cols, ldx, fmt, q, ldq, scales, qt, ldqt, scales_t, stream):
@@ -113,6 +131,12 @@ def fp8_block_scaled_gemm(M, N, K, a, lda, a_fmt, a_scales, b, ldb, b_fmt, b_lay
                           c, ldc, c_dtype, stream):
     return load_library().fp8_block_scaled_gemm(M, N, K, a, lda, a_fmt, a_scales, b, ldb, b_fmt, b_layout,
                                                  b_scales, b_scale_mode, c, ldc, c_dtype, stream)
+
+
+def fp8_gemm_f32s(M, N, K, a, lda, a_fmt, a_scales, b, ldb, b_fmt, b_layout, b_scales, b_scale_mode, c, ldc,
+                  c_dtype, stream):
+    return load_library().fp8_gemm_f32s(M, N, K, a, lda, a_fmt, a_scales, b, ldb, b_fmt, b_layout, b_scales,
+                                        b_scale_mode, c, ldc, c_dtype, stream)
 
 
 def mx_gemm(M, N, K, a, lda, a_fmt, a_scales, b, ldb, b_fmt, b_scales, c, ldc, c_dtype, stream):
@@ -201,6 +225,34 @@ def quantize_block(w, fmt=E4M3, stream=None):
     return q, s
 
 
+def quantize_token_f32s(x, fmt=E4M3, axis=ROW, stream=None):
+    """quantize_token with fp32 scales (float32 tensors in the same layouts)."""
+    torch = _torch()
+    rows, cols = x.shape
+    if axis == ROW:
+        q = _codes(rows, cols, x.device)
+        s = torch.empty((rows, (cols + 127) // 128), dtype=torch.float32, device=x.device)
+    else:
+        q = _codes(cols, rows, x.device)
+        s = torch.empty((cols, (rows + 127) // 128), dtype=torch.float32, device=x.device)
+    st = fp8_quantize_token_f32s(x.data_ptr(), _in_dtype(x), rows, cols, _ld(x), axis, fmt, q.data_ptr(), _ld(q),
+                                 s.data_ptr(), _stream(stream))
+    _check(st, "fp8_quantize_token_f32s")
+    return q, s
+
+
+def quantize_block_f32s(w, fmt=E4M3, stream=None):
+    """quantize_block with fp32 scales."""
+    torch = _torch()
+    rows, cols = w.shape
+    q = _codes(rows, cols, w.device)
+    s = torch.empty(((rows + 127) // 128, (cols + 127) // 128), dtype=torch.float32, device=w.device)
+    st = fp8_quantize_block_f32s(w.data_ptr(), _in_dtype(w), rows, cols, _ld(w), fmt, q.data_ptr(), _ld(q),
+                                 s.data_ptr(), _stream(stream))
+    _check(st, "fp8_quantize_block_f32s")
+    return q, s
+
+
 def quantize_token_dual(x, fmt=E4M3, stream=None):
     """Both token orientations from one read: (q, scales) as quantize_token ROW and
     (qt, scales_t) as quantize_token COL_T."""
@@ -274,4 +326,22 @@ def mx_scaled_gemm(a, a_scales, a_fmt, b, b_scales, b_fmt, out_dtype=None, out=N
     st = mx_gemm(M, N, K, a.data_ptr(), _ld(a), a_fmt, a_scales.data_ptr(), b.data_ptr(), _ld(b), b_fmt,
                  b_scales.data_ptr(), out.data_ptr(), _ld(out), c_dtype, _stream(stream))
     _check(st, "mx_gemm")
+    return out
+
+
+def gemm_f32s(a, a_scales, a_fmt, b, b_scales, b_fmt, b_layout=B_NK, b_scale_mode=SCALE_BLOCK128,
+              out_dtype=None, out=None, stream=None):
+    """block_scaled_gemm over operands with fp32 (float32 tensor) scales."""
+    torch = _torch()
+    M, K = a.shape
+    N = b.shape[0] if b_layout == B_NK else b.shape[1]
+    if out is None:
+        dt = torch.float32 if out_dtype in (None, torch.float32) else torch.bfloat16
+        buf = torch.empty((M, _pad16(max(N, 1))), dtype=dt, device=a.device)
+        out = buf[:, :N]
+    c_dtype = F32 if out.dtype == torch.float32 else BF16
+    st = fp8_gemm_f32s(M, N, K, a.data_ptr(), _ld(a), a_fmt, a_scales.data_ptr(), b.data_ptr(), _ld(b), b_fmt,
+                       b_layout, b_scales.data_ptr(), b_scale_mode, out.data_ptr(), _ld(out), c_dtype,
+                       _stream(stream))
+    _check(st, "fp8_gemm_f32s")
     return out

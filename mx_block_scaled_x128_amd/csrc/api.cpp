@@ -64,6 +64,36 @@ int fp8_quantize_block(const void* w, int w_dtype, int64_t rows, int64_t cols, i
   return launch_status();
 }
 
+int fp8_quantize_token_f32s(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                            int fmt, uint8_t* q, int64_t ldq, float* scales, void* stream) {
+  if (axis != MXFP8_GROUP_ROW && axis != MXFP8_GROUP_COL_T) return MXFP8_ERR_ENUM;
+  if (fmt != MXFP8_E4M3 && fmt != MXFP8_E5M2) return MXFP8_ERR_ENUM;
+  const int64_t q_row_len = axis == MXFP8_GROUP_ROW ? cols : rows;
+  int st = check_tensor_pair(x, x_dtype, rows, cols, ldx, q, ldq, q_row_len, scales);
+  if (st != MXFP8_OK || rows == 0 || cols == 0) return st;
+  if (cols % 16 != 0) return MXFP8_ERR_SHAPE;
+  if (axis == MXFP8_GROUP_COL_T && rows % 16 != 0) return MXFP8_ERR_SHAPE;
+  if ((uintptr_t)scales & 3) return MXFP8_ERR_ALIGN;
+  (void)hipGetLastError();
+  if (axis == MXFP8_GROUP_ROW)
+    mxfp8::launch_quant_row_f32s(x, x_dtype, rows, cols, ldx, fmt, q, ldq, scales, (hipStream_t)stream);
+  else
+    mxfp8::launch_quant_col_t_f32s(x, x_dtype, rows, cols, ldx, fmt, q, ldq, scales, (hipStream_t)stream);
+  return launch_status();
+}
+
+int fp8_quantize_block_f32s(const void* w, int w_dtype, int64_t rows, int64_t cols, int64_t ldw, int fmt,
+                            uint8_t* q, int64_t ldq, float* scales, void* stream) {
+  if (fmt != MXFP8_E4M3 && fmt != MXFP8_E5M2) return MXFP8_ERR_ENUM;
+  int st = check_tensor_pair(w, w_dtype, rows, cols, ldw, q, ldq, cols, scales);
+  if (st != MXFP8_OK || rows == 0 || cols == 0) return st;
+  if (cols % 16 != 0) return MXFP8_ERR_SHAPE;
+  if ((uintptr_t)scales & 3) return MXFP8_ERR_ALIGN;
+  (void)hipGetLastError();
+  mxfp8::launch_quant_block_f32s(w, w_dtype, rows, cols, ldw, fmt, q, ldq, scales, (hipStream_t)stream);
+  return launch_status();
+}
+
 namespace {
 // Checks shared by the two-orientation quantizers: both output pairs as for
 // the one-orientation calls, both extents multiples of 16, four distinct outputs.
@@ -145,6 +175,38 @@ int fp8_block_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int
   (void)hipGetLastError();
   mxfp8::launch_gemm(M, N, K, a, lda, a_fmt, a_scales, b, ldb, b_fmt, b_layout, b_scales, b_scale_mode, c, ldc,
                      c_dtype, (hipStream_t)stream);
+  return launch_status();
+}
+
+int fp8_gemm_f32s(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, int a_fmt, const float* a_scales,
+                  const uint8_t* b, int64_t ldb, int b_fmt, int b_layout, const float* b_scales, int b_scale_mode,
+                  void* c, int64_t ldc, int c_dtype, void* stream) {
+  if (a_fmt != MXFP8_E4M3 && a_fmt != MXFP8_E5M2) return MXFP8_ERR_ENUM;
+  if (b_fmt != MXFP8_E4M3 && b_fmt != MXFP8_E5M2) return MXFP8_ERR_ENUM;
+  if (b_layout != MXFP8_B_NK && b_layout != MXFP8_B_KN) return MXFP8_ERR_ENUM;
+  if (b_scale_mode != MXFP8_SCALE_BLOCK128 && b_scale_mode != MXFP8_SCALE_ROW128) return MXFP8_ERR_ENUM;
+  if (b_scale_mode == MXFP8_SCALE_ROW128 && b_layout != MXFP8_B_NK) return MXFP8_ERR_ENUM;
+  if (c_dtype != MXFP8_F32 && c_dtype != MXFP8_BF16) return MXFP8_ERR_ENUM;
+  if (M < 0 || N < 0 || K < 0) return MXFP8_ERR_SHAPE;
+  if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return MXFP8_ERR_SHAPE;
+  if (K % 128 != 0) return MXFP8_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXFP8_OK;
+  if (!c) return MXFP8_ERR_NULL;
+  if (K > 0 && (!a || !a_scales || !b || !b_scales)) return MXFP8_ERR_NULL;
+  if (ldc < N || ldc % 16 != 0) return MXFP8_ERR_LD;
+  if (K > 0) {
+    if (lda < K || lda % 16 != 0) return MXFP8_ERR_LD;
+    const int64_t b_row = b_layout == MXFP8_B_NK ? K : N;
+    if (ldb < b_row || ldb % 16 != 0) return MXFP8_ERR_LD;
+    if (!aligned16(a) || !aligned16(b)) return MXFP8_ERR_ALIGN;
+    if (((uintptr_t)a_scales & 3) || ((uintptr_t)b_scales & 3)) return MXFP8_ERR_ALIGN;
+  }
+  if (!aligned16(c)) return MXFP8_ERR_ALIGN;
+  if (c == (const void*)a || c == (const void*)b || c == (const void*)a_scales || c == (const void*)b_scales)
+    return MXFP8_ERR_ALIAS;
+  (void)hipGetLastError();
+  mxfp8::launch_gemm_f32s(M, N, K, a, lda, a_fmt, a_scales, b, ldb, b_fmt, b_layout, b_scales, b_scale_mode, c,
+                          ldc, c_dtype, (hipStream_t)stream);
   return launch_status();
 }
 

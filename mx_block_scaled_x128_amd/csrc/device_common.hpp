@@ -56,6 +56,17 @@ __device__ __forceinline__ float pow2_neg(int e) {
   return __uint_as_float((uint32_t)(127 - e) << 23);
 }
 
+// fp32 group scale of the "FP8 with an FP32 scale" variant (named as a
+// Table 4 variant on the review page of "A Comprehensive FP8 Training Recipe
+// for Reasoning-Enhanced Language Models", not defined there; read as):
+// amax / fmax in IEEE single precision (HIP's default division is the
+// correctly rounded one), 1 where that quotient rounds to zero.
+template <int FMT>
+__device__ __forceinline__ float scale_f32(uint32_t amax_bits) {
+  const float s = __uint_as_float(amax_bits) / FmtInfo<FMT>::fmax;
+  return s == 0.0f ? 1.0f : s;
+}
+
 // Four values -> four codes packed little-endian (a in the lowest byte).
 template <int FMT>
 __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {

@@ -137,7 +137,12 @@ __device__ __forceinline__ void mfma_retire_pad() {
 // MXS: MX operands -- scales per (row, 32-wide K block) for A ([M][K/32])
 // and for B stored [N][K] ([N][K/32]); otherwise one scale per 128-wide K
 // block (A [M][K/128]; B per row or per 128x128 tile of its storage).
-template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS>
+// F32S: those 128-wide block scales are fp32 values, not powers of two (the
+// "FP8 with an FP32 scale" variant): each K block's product runs through the
+// matrix cores with unit scales into a temporary tile, which is then added
+// into the accumulators times the block's scale product (one FMA per
+// element, with a per-column multiply when B's scales are per column).
+template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool F32S>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ SA,
     const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ SB, void* __restrict__ C,
@@ -146,6 +151,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int MT = WM / 32, NT = WN / 32;          // 32x32 MFMA tiles per wave
   static_assert(!MXS || (!BKN && BROW), "MX scales: B stored [N][K], scales per row");
+  static_assert(!F32S || (BM == 128 && BN == 128 && !MXS), "fp32 scales: 128x128 tiles");
+  // Scale values per B fragment held by a lane: one, except for fp32
+  // per-column scales, where a lane's 16 accumulator columns each have one.
+  constexpr int SBP = (F32S && BROW) ? 16 : 1;
   // LDS: two K-block buffers, each holding both 64-wide stages of one
   // 128-wide K block: the A tile [BM][128 B] and the B tile ([BN][128 B], or
   // [128 k][BN B] when B is [K][N]).  Whole 128-byte rows per load
@@ -244,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // Scale sources.  Group g's load instruction j of a wave (4 per operand)
   // covers entities e = 16 (4 wave + j) + (lane >> 2), K block 4g + (lane & 3)
   // (clamped to the last one; rows past M / N are clamped too).
-  const int srow = MXS ? 4 * nkb : nkb;  // scale bytes per row of A (and of per-row B scales)
+  const int srow = (MXS || F32S) ? 4 * nkb : nkb;  // scale bytes per row of A (and of per-row B scales)
   const uint8_t* sa_base = uniform_opaque(SA + (int64_t)m0 * srow);
   const uint8_t* sb_base = uniform_opaque(BROW ? SB + (int64_t)n0 * srow : SB);
   auto sdma_group = [&](int grp) __attribute__((always_inline)) {
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = (wave * 4 + j) * 16 + (lane >> 2);
-      if (MXS) {
+      if (MXS || F32S) {
         const uint32_t off = (uint32_t)(min(e, M - 1 - m0) * srow + 4 * kbs);
         __builtin_amdgcn_global_load_lds(sa_base + off, area + (wave * 4 + j) * 256, 4, 0, 0);
       } else {
@@ -264,8 +273,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = (wave * 4 + j) * 16 + (lane >> 2);
-      if (MXS) {
+      if (MXS || (F32S && BROW)) {
         const uint32_t off = (uint32_t)(min(e, N - 1 - n0) * srow + 4 * kbs);
+        __builtin_amdgcn_global_load_lds(sb_base + off, area + SG_OP + (wave * 4 + j) * 256, 4, 0, 0);
+      } else if (F32S) {
+        const int nb = min((n0 + e) >> 7, nnb - 1);
+        const uint32_t off = (uint32_t)(4 * (BKN ? kbs * nnb + nb : nb * nkb + kbs));
         __builtin_amdgcn_global_load_lds(sb_base + off, area + SG_OP + (wave * 4 + j) * 256, 4, 0, 0);
       } else {
         uint32_t off;
@@ -314,16 +327,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   const int g = lane >> 5;
   const uint32_t sa_rd = opaque((wm * WM + (lane & 31)) * 16 + (MXS ? 2 * g : 0));
   const uint32_t sb_rd = opaque(SG_OP + (wn * WN + (lane & 31)) * 16 + (MXS ? 2 * g : 0));
-  auto read_scales = [&](int kb, int (&sa)[MT], int (&sb)[NT]) __attribute__((always_inline)) {
+  // With F32S and per-column B scales, lane half g reads the scales of its
+  // 16 accumulator columns 8q + 4g + j (q, j = 0..3) of each fragment.
+  const uint32_t sbc_rd = opaque(SG_OP + (wn * WN + 4 * g) * 16);
+  auto read_scales = [&](int kb, int (&sa)[MT], int (&sb)[NT * SBP]) __attribute__((always_inline)) {
     const uint8_t* area = sgrp + ((kb >> 2) & 1) * SG + (kb & 3) * 4;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
       sa[mt] = MXS ? (int)*reinterpret_cast<const uint16_t*>(area + sa_rd + mt * 512)
                    : *reinterpret_cast<const int*>(area + sa_rd + mt * 512);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      sb[nt] = MXS ? (int)*reinterpret_cast<const uint16_t*>(area + sb_rd + nt * 512)
-                   : *reinterpret_cast<const int*>(area + sb_rd + nt * 512);
+    for (int nt = 0; nt < NT; ++nt) {
+      if constexpr (SBP == 16) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sb[nt * 16 + r] = *reinterpret_cast<const int*>(area + sbc_rd + (nt * 32 + 8 * (r >> 2) + (r & 3)) * 16);
+      } else {
+        sb[nt] = MXS ? (int)*reinterpret_cast<const uint16_t*>(area + sb_rd + nt * 512)
+                     : *reinterpret_cast<const int*>(area + sb_rd + nt * 512);
+      }
+    }
   };
 
   v16f acc[MT][NT];
@@ -333,6 +356,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.0f;
+  // F32S: each K block's unscaled product, per fragment pair.
+  constexpr int TM = F32S ? MT : 1, TN = F32S ? NT : 1;
+  v16f tmp[TM][TN];
+#pragma unroll
+  for (int mt = 0; mt < TM; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < TN; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmp[mt][nt][i] = 0.0f;
+  // F32S: acc[mt][nt] += tmp[mt][nt] * (block scale of the row x that of
+  // each column).  Lane l's 16 accumulators of a fragment pair are row l & 31
+  // and columns 8q + 4(l >> 5) + j of the 32x32 block (register 4q + j).
+  auto apply = [&](int mt, int nt, const int (&ps_a)[MT], const int (&ps_b)[NT * SBP])
+                   __attribute__((always_inline)) {
+    if constexpr (F32S) {
+      const float fa = __int_as_float(ps_a[mt]);
+      if constexpr (SBP == 16) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[mt][nt][r] = __builtin_fmaf(tmp[mt][nt][r], fa * __int_as_float(ps_b[nt * 16 + r]), acc[mt][nt][r]);
+      } else {
+        const float f = fa * __int_as_float(ps_b[nt]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mt][nt][r] = __builtin_fmaf(tmp[mt][nt][r], f, acc[mt][nt][r]);
+      }
+    }
+  };
 
   // Fragments of one 64-wide stage (half h of a K block).  Lane l holds, for
   // its row (A) / column (B) l & 31, 32 K bytes as two 16-byte parts (its
@@ -427,21 +477,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // rd_p >= 0: read the fragments of stage half rd_h of buffer rd_p into
   // (na, nb); with do_sc also K block sc_kb's scales into (nsa, nsb).
   // grp >= 0: load scale group grp.
+  // F32S: the first stage of a K block first adds the previous K block's
+  // temporaries into the accumulators (with that block's scales, still in
+  // (nsa, nsb) until this block's second stage reads the next ones), one
+  // fragment pair before each MFMA that overwrites its temporary; at least
+  // three MFMAs separate each temporary's last write from that read.
   auto stage = [&](int cur_h, int dma_p, int dma_kb, int rd_p, int rd_h, bool do_sc, int sc_kb, int grp,
                    const v8i (&ca)[MT],
                    const v8i (&cb)[NT], v8i (&na)[MT], v8i (&nb)[NT], const int (&csa)[MT],
-                   const int (&csb)[NT], int (&nsa)[MT], int (&nsb)[NT]) __attribute__((always_inline)) {
+                   const int (&csb)[NT * SBP], int (&nsa)[MT], int (&nsb)[NT * SBP]) __attribute__((always_inline)) {
     Src src = {nullptr, nullptr};
     if (dma_p >= 0) src = dma_src(dma_kb);
 #pragma unroll
     for (int i = 0; i < MFMAS; ++i) {
       const int mt = i / NT, nt = i % NT;
-      if (MXS && cur_h == 1)
+      if constexpr (F32S) {
+        if (cur_h == 0) {
+          apply(mt, nt, nsa, nsb);
+          tmp[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[nt], ca[mt], v16f{}, BFMT, AFMT, 0,
+                                                                       127, 0, 127);
+        } else {
+          tmp[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[nt], ca[mt], tmp[mt][nt], BFMT, AFMT,
+                                                                       0, 127, 0, 127);
+        }
+      } else if (MXS && cur_h == 1) {
         acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[nt], ca[mt], acc[mt][nt], BFMT, AFMT, 1,
                                                                      csb[nt], 1, csa[mt]);
-      else
+      } else {
         acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[nt], ca[mt], acc[mt][nt], BFMT, AFMT, 0,
                                                                      csb[nt], 0, csa[mt]);
+      }
       if (rd_p >= 0 && do_sc && i == 0) read_scales(sc_kb, nsa, nsb);
       if (grp >= 0 && i == 0) sdma_group(grp);  // after the scale read: same array
 #pragma unroll
@@ -457,7 +522,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // Two register sets each for fragments (stage parity) and scales (K block
   // parity); the code below alternates them, so nothing is copied.
   v8i fa0[MT], fb0[NT], fa1[MT], fb1[NT];
-  int sa0[MT], sb0[NT], sa1[MT], sb1[NT];
+  int sa0[MT], sb0[NT * SBP], sa1[MT], sb1[NT * SBP];
+  if constexpr (F32S) {  // the "previous K block" of the first one: zero temporaries, zero scales
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) sa1[mt] = 0;
+#pragma unroll
+    for (int i = 0; i < NT * SBP; ++i) sb1[i] = 0;
+  }
 
   // ---- schedule.  Each K block's first stage
   // multiplies while the second stage's fragments are read.  At the top of
@@ -474,8 +545,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // kb = 2 mod 4 the same bytes are written again (harmless, and no branch
   // in the instruction stream); a group past the last K block loads clamped
   // bytes nobody reads.  A group is read from 2 to 3 K blocks later on.
-  auto kblock = [&](int p, int kb, bool dma, bool next, bool sg, const int (&csa)[MT], const int (&csb)[NT],
-                    int (&nsa)[MT], int (&nsb)[NT]) __attribute__((always_inline)) {
+  auto kblock = [&](int p, int kb, bool dma, bool next, bool sg, const int (&csa)[MT], const int (&csb)[NT * SBP],
+                    int (&nsa)[MT], int (&nsb)[NT * SBP]) __attribute__((always_inline)) {
     stage(0, -1, 0, p, 1, false, 0, -1, fa0, fb0, fa1, fb1, csa, csb, nsa, nsb);
     if (dma || next) wait_vm_barrier<0>();
     stage(1, dma ? p : -1, kb + 2, next ? (p ^ 1) : -1, 0, next, kb + 1, sg ? (kb >> 2) + 1 : -1, fa1, fb1, fa0,
@@ -511,20 +582,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   }
   if (kb < main_kb) {
     kblock(0, kb, true, true, false, sa0, sb0, sa1, sb1);
+    // The drain takes K block kb + 1's scales from set 0; with F32S set 1
+    // must then hold K block kb's (its temporaries are added in the drain).
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) sa0[mt] = sa1[mt];
+    for (int mt = 0; mt < MT; ++mt) {
+      const int t = sa0[mt];
+      sa0[mt] = sa1[mt];
+      if (F32S) sa1[mt] = t;
+    }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sb0[nt] = sb1[nt];
+    for (int i = 0; i < NT * SBP; ++i) {
+      const int t = sb0[i];
+      sb0[i] = sb1[i];
+      if (F32S) sb1[i] = t;
+    }
   }
 
   // Pins the accumulators to AGPRs where the K loop ends: left free, the
   // allocator moves some of them into VGPRs during the drain (the epilogue
   // reads them through VALU) and spills fragments to make room.
   auto pin_acc = [&]() __attribute__((always_inline)) {
+    if constexpr (!F32S) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+a"(acc[mt][nt]));
+    }
+  };
+  // F32S: the last K block's temporaries, after the retire pad.
+  auto apply_all = [&](const int (&ps_a)[MT], const int (&ps_b)[NT * SBP]) __attribute__((always_inline)) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+a"(acc[mt][nt]));
+      for (int nt = 0; nt < NT; ++nt) apply(mt, nt, ps_a, ps_b);
   };
 
   // ---- epilogue.  Lane l holds, for each (mt, nt), C[r][c .. c+3] with
@@ -621,11 +711,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
     kblock(p, nkb - 2, false, true, false, sa0, sb0, sa1, sb1);
     kblock(p ^ 1, nkb - 1, false, false, false, sa1, sb1, sa0, sb0);
     mfma_retire_pad();
+    apply_all(sa1, sb1);
     pin_acc();
     epilogue(buf_ptr(p));
   } else if (BM < 256 && nkb == 1) {  // the 256-wide tile is launched with K >= 256 only
     kblock(0, 0, false, false, false, sa0, sb0, sa1, sb1);
     mfma_retire_pad();
+    apply_all(sa0, sb0);
     pin_acc();
     epilogue(kbuf1);  // never loaded when K = 128
   } else if (BM < 256) {
@@ -634,12 +726,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
 #endif
 }
 
-template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS>
+template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool F32S = false>
 void launch_tile(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
                  const uint8_t* b, int64_t ldb, const uint8_t* sb, void* c, int64_t ldc, int c_dtype,
                  int tiles_m, int tiles_n, int tile_first, int cells, int split, hipStream_t stream) {
   if (cells <= 0) return;
-  hipLaunchKernelGGL((gemm_bs_kernel<BM, BN, STAGES, AFMT, BFMT, BKN, BROW, MXS>), dim3(cells << (2 * split)),
+  hipLaunchKernelGGL((gemm_bs_kernel<BM, BN, STAGES, AFMT, BFMT, BKN, BROW, MXS, F32S>), dim3(cells << (2 * split)),
                      dim3(kThreads), 0, stream, (int)M, (int)N, (int)K, a, lda, sa, b, ldb, sb, c, ldc,
                      c_dtype == 1 ? 1 : 0, tiles_m, tiles_n, tile_first, split);
 }
@@ -703,9 +795,42 @@ void launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, 
     launch_shape<AFMT, BFMT, false, false, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
 }
 
+// fp32 block scales: 128x128 tiles only (the temporaries double the
+// accumulator registers).
+template <int AFMT, int BFMT>
+void launch_f32s_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
+                     const uint8_t* b, int64_t ldb, int b_layout, const uint8_t* sb, int b_scale_mode, void* c,
+                     int64_t ldc, int c_dtype, hipStream_t stream) {
+  const int sm = (int)((M + 127) / 128), sn = (int)((N + 127) / 128);
+  if (b_layout == 1)
+    launch_tile<128, 128, 4, AFMT, BFMT, true, false, false, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype,
+                                                                  sm, sn, 0, sm * sn, 0, stream);
+  else if (b_scale_mode == 1)
+    launch_tile<128, 128, 4, AFMT, BFMT, false, true, false, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype,
+                                                                  sm, sn, 0, sm * sn, 0, stream);
+  else
+    launch_tile<128, 128, 4, AFMT, BFMT, false, false, false, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc,
+                                                                   c_dtype, sm, sn, 0, sm * sn, 0, stream);
+}
+
 }  // namespace gemm_detail
 
 using namespace gemm_detail;
+
+void launch_gemm_f32s(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, int a_fmt,
+                      const float* sa, const uint8_t* b, int64_t ldb, int b_fmt, int b_layout, const float* sb,
+                      int b_scale_mode, void* c, int64_t ldc, int c_dtype, hipStream_t stream) {
+  const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
+  const uint8_t* sb8 = reinterpret_cast<const uint8_t*>(sb);
+  if (a_fmt == 0 && b_fmt == 0)
+    launch_f32s_fmt<0, 0>(M, N, K, a, lda, sa8, b, ldb, b_layout, sb8, b_scale_mode, c, ldc, c_dtype, stream);
+  else if (a_fmt == 1 && b_fmt == 0)
+    launch_f32s_fmt<1, 0>(M, N, K, a, lda, sa8, b, ldb, b_layout, sb8, b_scale_mode, c, ldc, c_dtype, stream);
+  else if (a_fmt == 0 && b_fmt == 1)
+    launch_f32s_fmt<0, 1>(M, N, K, a, lda, sa8, b, ldb, b_layout, sb8, b_scale_mode, c, ldc, c_dtype, stream);
+  else
+    launch_f32s_fmt<1, 1>(M, N, K, a, lda, sa8, b, ldb, b_layout, sb8, b_scale_mode, c, ldc, c_dtype, stream);
+}
 
 void launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, int a_fmt,
                  const uint8_t* sa, const uint8_t* b, int64_t ldb, int b_fmt, int b_layout,

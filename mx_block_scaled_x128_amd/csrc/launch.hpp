@@ -16,6 +16,13 @@ void launch_quant_col_t(const void* x, int dtype, int64_t rows, int64_t cols, in
 // 128x128 tiles.  cols % 16 == 0.
 void launch_quant_block(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw, int fmt,
                         uint8_t* q, int64_t ldq, uint8_t* s, hipStream_t stream);
+// fp32-scale variants of the three above (scales as floats, same layouts).
+void launch_quant_row_f32s(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                           uint8_t* q, int64_t ldq, float* s, hipStream_t stream);
+void launch_quant_col_t_f32s(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                             uint8_t* qt, int64_t ldq, float* st, hipStream_t stream);
+void launch_quant_block_f32s(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw, int fmt,
+                             uint8_t* q, int64_t ldq, float* s, hipStream_t stream);
 // Both token orientations from one read: row groups (q, s) and transposed
 // column groups (qt, st).  rows % 16 == 0, cols % 16 == 0.
 void launch_quant_dual(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
@@ -33,6 +40,12 @@ void launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
                  const uint8_t* sa, const uint8_t* b, int64_t ldb, int b_fmt, int b_layout,
                  const uint8_t* sb, int b_scale_mode, void* c, int64_t ldc, int c_dtype,
                  hipStream_t stream);
+
+// The block-scaled GEMM with fp32 scales (same layouts, floats).  K % 128 == 0,
+// scale pointers 4-byte aligned.
+void launch_gemm_f32s(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, int a_fmt,
+                      const float* sa, const uint8_t* b, int64_t ldb, int b_fmt, int b_layout, const float* sb,
+                      int b_scale_mode, void* c, int64_t ldc, int c_dtype, hipStream_t stream);
 
 // MX GEMM: A [M][K] with scales [M][K/32], B [N][K] with scales [N][K/32].
 // K % 128 == 0, M, N >= 1, scale pointers 4-byte aligned.

@@ -34,133 +34,26 @@ __device__ __forceinline__ uint2 codes8(const float (&f)[8], float sc) {
   return o;
 }
 
-// ---------------------------------------------------------------------------
-// 1x128 groups along rows.  A wavefront handles "items" of 4 consecutive
-// groups of one row: 16 lanes per group, 8 elements per lane.  Items are
-// wave-uniform, so the row / column split runs on the scalar unit.
-// ---------------------------------------------------------------------------
-template <typename InT, int FMT, int U>
-__global__ __launch_bounds__(kThreads) void quant_row_kernel(
-    const InT* __restrict__ x, uint32_t cols, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
-    uint8_t* __restrict__ s, uint32_t ngroups, uint32_t ipr, uint32_t total_items) {
-  const uint32_t lane = threadIdx.x & 63;
-  const uint32_t sub = lane & 15;
-  const uint32_t slot = lane >> 4;
-  const uint32_t wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  const uint32_t nwaves = gridDim.x * (kThreads / 64);
-  for (uint32_t it = wave * U; it < total_items; it += nwaves * U) {
-    float f[U][8];
-    uint32_t row[U], grp[U];
-    bool act[U], gvalid[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t item = it + u;
-      const uint32_t r = item / ipr;
-      const uint32_t g = (item - r * ipr) * 4 + slot;
-      const uint32_t c = g * 128 + sub * 8;
-      row[u] = r;
-      grp[u] = g;
-      gvalid[u] = item < total_items && g < ngroups;
-      act[u] = gvalid[u] && c < cols;
-      if (act[u]) load8<true>(x + (int64_t)r * ldx + c, f[u]);
-      else zero8(f[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      uint32_t m = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) m = max(m, abs_bits(f[u][j]));
-      m = max_row16(m);
-      const int e = scale_exp_ceil<FMT>(m);
-      const float sc = pow2_neg(e);
-      if (act[u])
-        store_nt(q + (int64_t)row[u] * ldq + grp[u] * 128 + sub * 8, codes8<FMT>(f[u], sc));
-      if (sub == 0 && gvalid[u]) s[(int64_t)row[u] * ngroups + grp[u]] = (uint8_t)(e + 127);
-    }
-  }
+// Eight codes under an fp32 scale: the fp32 quotient x / s (IEEE division),
+// clamped to +-fmax (the saturation of the cast; quotients can exceed fmax by
+// the rounding of s), then the hardware RNE cast.
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt4_div(float a, float b, float c, float d, float s) {
+  constexpr float fmax = FmtInfo<FMT>::fmax;
+  return cvt4<FMT>(__builtin_amdgcn_fmed3f(a / s, -fmax, fmax), __builtin_amdgcn_fmed3f(b / s, -fmax, fmax),
+                   __builtin_amdgcn_fmed3f(c / s, -fmax, fmax), __builtin_amdgcn_fmed3f(d / s, -fmax, fmax));
+}
+template <int FMT>
+__device__ __forceinline__ uint2 codes8_div(const float (&f)[8], float s) {
+  uint2 o;
+  o.x = cvt4_div<FMT>(f[0], f[1], f[2], f[3], s);
+  o.y = cvt4_div<FMT>(f[4], f[5], f[6], f[7], s);
+  return o;
 }
 
-// ---------------------------------------------------------------------------
-// 128-token groups down columns, codes written transposed (token axis
-// contiguous).  One workgroup per 128 tokens x 128 channels tile: each thread
-// holds 8 tokens x 8 channels in registers; column maxima reduce over the 8
-// lanes of a wave that share a channel chunk (DPP), then over the two waves
-// that cover the tile's token halves (LDS).  Codes are transposed through an
-// LDS tile whose rows are padded to 136 bytes so that the 8-byte writes of a
-// wavefront fall on distinct banks.
-// ---------------------------------------------------------------------------
+// Row pitch of the transposed code tiles in LDS (bytes); see quant_col_t_kernel.
 constexpr int kColPitch = 136;
 
-template <typename InT, int FMT>
-__global__ __launch_bounds__(kThreads) void quant_col_t_kernel(
-    const InT* __restrict__ x, uint32_t rows, uint32_t cols, int64_t ldx, uint8_t* __restrict__ qt,
-    int64_t ldq, uint8_t* __restrict__ st, uint32_t ngt) {
-  __shared__ uint32_t red[2][128];
-  __shared__ int exps[128];
-  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * kColPitch];
-  const uint32_t tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const uint32_t tr = (lane & 7) + 8 * (w & 1);   // token chunk: tokens tr*8 .. tr*8+7
-  const uint32_t tc = (lane >> 3) + 8 * (w >> 1); // channel chunk: channels tc*8 .. tc*8+7
-  const uint32_t c0 = blockIdx.x * 128, t0 = blockIdx.y * 128;
-  const bool cact = c0 + tc * 8 < cols;
-  float f[8][8];  // [token][channel]
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t r = t0 + tr * 8 + i;
-    if (cact && r < rows) load8<false>(x + (int64_t)r * ldx + c0 + tc * 8, f[i]);
-    else zero8(f[i]);
-  }
-  uint32_t m[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t a = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a = max(a, abs_bits(f[i][j]));
-    m[j] = max_oct(a);
-  }
-  if ((lane & 7) == 0) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) red[w & 1][tc * 8 + j] = m[j];
-  }
-  __syncthreads();
-  if (tid < 128) {
-    const uint32_t a = max(red[0][tid], red[1][tid]);
-    const int e = scale_exp_ceil<FMT>(a);
-    exps[tid] = e;
-    if (c0 + tid < cols) st[(int64_t)(c0 + tid) * ngt + blockIdx.y] = (uint8_t)(e + 127);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float sc = pow2_neg(exps[tc * 8 + j]);
-    uint2 o;
-    o.x = cvt4<FMT>(f[0][j] * sc, f[1][j] * sc, f[2][j] * sc, f[3][j] * sc);
-    o.y = cvt4<FMT>(f[4][j] * sc, f[5][j] * sc, f[6][j] * sc, f[7][j] * sc);
-    *reinterpret_cast<uint2*>(tile + (tc * 8 + j) * kColPitch + tr * 8) = o;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int rep = 0; rep < 4; ++rep) {
-    const uint32_t idx = rep * kThreads + tid;
-    const uint32_t ch = idx >> 3, ck = idx & 7;
-    if (c0 + ch < cols && t0 + ck * 16 < rows) {
-      const uint2 a = *reinterpret_cast<const uint2*>(tile + ch * kColPitch + ck * 16);
-      const uint2 b = *reinterpret_cast<const uint2*>(tile + ch * kColPitch + ck * 16 + 8);
-      store_nt(qt + (int64_t)(c0 + ch) * ldq + t0 + ck * 16, make_uint4(a.x, a.y, b.x, b.y));
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Both orientations of the token-wise quantization from one read of x: the
-// 1x128 row groups (codes in x's layout) and the 128-token column groups
-// (codes transposed).  The tile and thread layout are those of
-// quant_col_t_kernel; a tile's 128 channels are exactly one row group of each
-// of its 128 tokens (tiles start on multiples of 128), so each token's row
-// maximum reduces over the 8 lanes of a wave that share its token chunk
-// (stride-8 lanes) and then over the two waves that cover the tile's channel
-// halves (LDS).  Both code sets are staged in LDS and stored as whole rows.
-// ---------------------------------------------------------------------------
 // A 128 x 128-byte tile of codes in LDS in the layout of the output (rows of
 // 128 bytes, no padding): the 8-byte chunk c of row r sits in 16-byte slot
 // (c >> 1) ^ ((r >> 3) & 7), half c & 1.  Writers (lane = row chunk r >> 3,
@@ -200,6 +93,144 @@ __device__ __forceinline__ void store_tile_t(const uint8_t* tile, uint8_t* __res
   }
 }
 
+// ---------------------------------------------------------------------------
+// 1x128 groups along rows.  A wavefront handles "items" of 4 consecutive
+// groups of one row: 16 lanes per group, 8 elements per lane.  Items are
+// wave-uniform, so the row / column split runs on the scalar unit.
+// ---------------------------------------------------------------------------
+// F32S: fp32 scales (scale_f32, codes8_div) instead of E8M0 bytes; s then
+// points to floats.
+template <typename InT, int FMT, int U, bool F32S>
+__global__ __launch_bounds__(kThreads) void quant_row_kernel(
+    const InT* __restrict__ x, uint32_t cols, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+    void* __restrict__ s, uint32_t ngroups, uint32_t ipr, uint32_t total_items) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t sub = lane & 15;
+  const uint32_t slot = lane >> 4;
+  const uint32_t wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const uint32_t nwaves = gridDim.x * (kThreads / 64);
+  for (uint32_t it = wave * U; it < total_items; it += nwaves * U) {
+    float f[U][8];
+    uint32_t row[U], grp[U];
+    bool act[U], gvalid[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t item = it + u;
+      const uint32_t r = item / ipr;
+      const uint32_t g = (item - r * ipr) * 4 + slot;
+      const uint32_t c = g * 128 + sub * 8;
+      row[u] = r;
+      grp[u] = g;
+      gvalid[u] = item < total_items && g < ngroups;
+      act[u] = gvalid[u] && c < cols;
+      if (act[u]) load8<true>(x + (int64_t)r * ldx + c, f[u]);
+      else zero8(f[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = max(m, abs_bits(f[u][j]));
+      m = max_row16(m);
+      if constexpr (F32S) {
+        const float sf = scale_f32<FMT>(m);
+        if (act[u])
+          store_nt(q + (int64_t)row[u] * ldq + grp[u] * 128 + sub * 8, codes8_div<FMT>(f[u], sf));
+        if (sub == 0 && gvalid[u]) static_cast<float*>(s)[(int64_t)row[u] * ngroups + grp[u]] = sf;
+      } else {
+        const int e = scale_exp_ceil<FMT>(m);
+        const float sc = pow2_neg(e);
+        if (act[u])
+          store_nt(q + (int64_t)row[u] * ldq + grp[u] * 128 + sub * 8, codes8<FMT>(f[u], sc));
+        if (sub == 0 && gvalid[u]) static_cast<uint8_t*>(s)[(int64_t)row[u] * ngroups + grp[u]] = (uint8_t)(e + 127);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128-token groups down columns, codes written transposed (token axis
+// contiguous).  One workgroup per 128 tokens x 128 channels tile: each thread
+// holds 8 tokens x 8 channels in registers; column maxima reduce over the 8
+// lanes of a wave that share a channel chunk (DPP), then over the two waves
+// that cover the tile's token halves (LDS).  Codes are transposed through an
+// LDS tile whose rows are padded to 136 bytes so that the 8-byte writes of a
+// wavefront fall on distinct banks.
+// ---------------------------------------------------------------------------
+
+template <typename InT, int FMT, bool F32S>
+__global__ __launch_bounds__(kThreads) void quant_col_t_kernel(
+    const InT* __restrict__ x, uint32_t rows, uint32_t cols, int64_t ldx, uint8_t* __restrict__ qt,
+    int64_t ldq, void* __restrict__ st, uint32_t ngt) {
+  __shared__ uint32_t red[2][128];
+  __shared__ int exps[128];  // exponents, or with F32S the fp32 scales' bits
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * kColPitch];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint32_t tr = (lane & 7) + 8 * (w & 1);   // token chunk: tokens tr*8 .. tr*8+7
+  const uint32_t tc = (lane >> 3) + 8 * (w >> 1); // channel chunk: channels tc*8 .. tc*8+7
+  const uint32_t c0 = blockIdx.x * 128, t0 = blockIdx.y * 128;
+  const bool cact = c0 + tc * 8 < cols;
+  float f[8][8];  // [token][channel]
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t r = t0 + tr * 8 + i;
+    if (cact && r < rows) load8<false>(x + (int64_t)r * ldx + c0 + tc * 8, f[i]);
+    else zero8(f[i]);
+  }
+  uint32_t m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t a = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = max(a, abs_bits(f[i][j]));
+    m[j] = max_oct(a);
+  }
+  if ((lane & 7) == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[w & 1][tc * 8 + j] = m[j];
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const uint32_t a = max(red[0][tid], red[1][tid]);
+    if constexpr (F32S) {
+      const float sf = scale_f32<FMT>(a);
+      exps[tid] = __float_as_int(sf);
+      if (c0 + tid < cols) static_cast<float*>(st)[(int64_t)(c0 + tid) * ngt + blockIdx.y] = sf;
+    } else {
+      const int e = scale_exp_ceil<FMT>(a);
+      exps[tid] = e;
+      if (c0 + tid < cols) static_cast<uint8_t*>(st)[(int64_t)(c0 + tid) * ngt + blockIdx.y] = (uint8_t)(e + 127);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint2 o;
+    if constexpr (F32S) {
+      const float sf = __int_as_float(exps[tc * 8 + j]);
+      o.x = cvt4_div<FMT>(f[0][j], f[1][j], f[2][j], f[3][j], sf);
+      o.y = cvt4_div<FMT>(f[4][j], f[5][j], f[6][j], f[7][j], sf);
+    } else {
+      const float sc = pow2_neg(exps[tc * 8 + j]);
+      o.x = cvt4<FMT>(f[0][j] * sc, f[1][j] * sc, f[2][j] * sc, f[3][j] * sc);
+      o.y = cvt4<FMT>(f[4][j] * sc, f[5][j] * sc, f[6][j] * sc, f[7][j] * sc);
+    }
+    *reinterpret_cast<uint2*>(tile + (tc * 8 + j) * kColPitch + tr * 8) = o;
+  }
+  __syncthreads();
+  store_tile_t(tile, qt, ldq, c0, t0, cols, rows, tid);
+}
+
+// ---------------------------------------------------------------------------
+// Both orientations of the token-wise quantization from one read of x: the
+// 1x128 row groups (codes in x's layout) and the 128-token column groups
+// (codes transposed).  The tile and thread layout are those of
+// quant_col_t_kernel; a tile's 128 channels are exactly one row group of each
+// of its 128 tokens (tiles start on multiples of 128), so each token's row
+// maximum reduces over the 8 lanes of a wave that share its token chunk
+// (stride-8 lanes) and then over the two waves that cover the tile's channel
+// halves (LDS).  Both code sets are staged in LDS and stored as whole rows.
+// ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t max_stride8(uint32_t v) {
   v = dpp_max<DPP_ROW_ROR8>(v);
   uint32_t o = (uint32_t)__shfl_xor((int)v, 16);
@@ -347,10 +378,10 @@ __global__ __launch_bounds__(kThreads) void quant_block_dual_kernel(
 // each wavefront and 4 values through LDS across wavefronts; then one pass of
 // casts and 8-byte stores.  Input is read from HBM exactly once.
 // ---------------------------------------------------------------------------
-template <typename InT, int FMT>
+template <typename InT, int FMT, bool F32S>
 __global__ __launch_bounds__(kThreads) void quant_block_kernel(
     const InT* __restrict__ w, uint32_t rows, uint32_t cols, int64_t ldw, uint8_t* __restrict__ q,
-    int64_t ldq, uint8_t* __restrict__ s, uint32_t nbc) {
+    int64_t ldq, void* __restrict__ s, uint32_t nbc) {
   __shared__ uint32_t red[4];
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t tc = lane & 15;               // column chunk: columns tc*8 .. tc*8+7
@@ -373,15 +404,24 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(
   if (lane == 0) red[wv] = m;
   __syncthreads();
   m = max(max(red[0], red[1]), max(red[2], red[3]));
-  const int e = scale_exp_ceil<FMT>(m);
-  const float sc = pow2_neg(e);
+  if constexpr (F32S) {
+    const float sf = scale_f32<FMT>(m);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t r = r0 + tr * 8 + i;
-    if (cact && r < rows)
-      store_nt(q + (int64_t)r * ldq + c0 + tc * 8, codes8<FMT>(f[i], sc));
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t r = r0 + tr * 8 + i;
+      if (cact && r < rows) store_nt(q + (int64_t)r * ldq + c0 + tc * 8, codes8_div<FMT>(f[i], sf));
+    }
+    if (tid == 0) static_cast<float*>(s)[(int64_t)blockIdx.y * nbc + blockIdx.x] = sf;
+  } else {
+    const int e = scale_exp_ceil<FMT>(m);
+    const float sc = pow2_neg(e);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t r = r0 + tr * 8 + i;
+      if (cact && r < rows) store_nt(q + (int64_t)r * ldq + c0 + tc * 8, codes8<FMT>(f[i], sc));
+    }
+    if (tid == 0) static_cast<uint8_t*>(s)[(int64_t)blockIdx.y * nbc + blockIdx.x] = (uint8_t)(e + 127);
   }
-  if (tid == 0) s[(int64_t)blockIdx.y * nbc + blockIdx.x] = (uint8_t)(e + 127);
 }
 
 // ---------------------------------------------------------------------------
@@ -460,46 +500,68 @@ using namespace quant_detail;
 
 // ----------------------------------------------------------------- launchers
 
-template <typename InT, int FMT>
+template <typename InT, int FMT, bool F32S>
 static void row_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* q,
-                         int64_t ldq, uint8_t* s, hipStream_t st) {
+                         int64_t ldq, void* s, hipStream_t st) {
   constexpr int U = 2;
   const uint32_t ngroups = (uint32_t)((cols + 127) / 128);
   const uint32_t ipr = (ngroups + 3) / 4;
   const uint64_t items = (uint64_t)rows * ipr;
-  hipLaunchKernelGGL((quant_row_kernel<InT, FMT, U>), dim3(grid_for(items, U)), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL((quant_row_kernel<InT, FMT, U, F32S>), dim3(grid_for(items, U)), dim3(kThreads), 0, st,
                      (const InT*)x, (uint32_t)cols, ldx, q, ldq, s, ngroups, ipr, (uint32_t)items);
+}
+
+template <bool F32S>
+static void row_any(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
+                    int64_t ldq, void* s, hipStream_t st) {
+  if (dtype == 1) {
+    if (fmt == 0) row_dispatch<uint16_t, 0, F32S>(x, rows, cols, ldx, q, ldq, s, st);
+    else row_dispatch<uint16_t, 1, F32S>(x, rows, cols, ldx, q, ldq, s, st);
+  } else {
+    if (fmt == 0) row_dispatch<float, 0, F32S>(x, rows, cols, ldx, q, ldq, s, st);
+    else row_dispatch<float, 1, F32S>(x, rows, cols, ldx, q, ldq, s, st);
+  }
 }
 
 void launch_quant_row(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                       uint8_t* q, int64_t ldq, uint8_t* s, hipStream_t st) {
-  if (dtype == 1) {
-    if (fmt == 0) row_dispatch<uint16_t, 0>(x, rows, cols, ldx, q, ldq, s, st);
-    else row_dispatch<uint16_t, 1>(x, rows, cols, ldx, q, ldq, s, st);
-  } else {
-    if (fmt == 0) row_dispatch<float, 0>(x, rows, cols, ldx, q, ldq, s, st);
-    else row_dispatch<float, 1>(x, rows, cols, ldx, q, ldq, s, st);
-  }
+  row_any<false>(x, dtype, rows, cols, ldx, fmt, q, ldq, s, st);
 }
 
-template <typename InT, int FMT>
+void launch_quant_row_f32s(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                           uint8_t* q, int64_t ldq, float* s, hipStream_t st) {
+  row_any<true>(x, dtype, rows, cols, ldx, fmt, q, ldq, s, st);
+}
+
+template <typename InT, int FMT, bool F32S>
 static void col_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* qt,
-                         int64_t ldq, uint8_t* st, hipStream_t stream) {
+                         int64_t ldq, void* st, hipStream_t stream) {
   const uint32_t ngt = (uint32_t)((rows + 127) / 128);
   const dim3 grid((uint32_t)((cols + 127) / 128), ngt);
-  hipLaunchKernelGGL((quant_col_t_kernel<InT, FMT>), grid, dim3(kThreads), 0, stream, (const InT*)x,
+  hipLaunchKernelGGL((quant_col_t_kernel<InT, FMT, F32S>), grid, dim3(kThreads), 0, stream, (const InT*)x,
                      (uint32_t)rows, (uint32_t)cols, ldx, qt, ldq, st, ngt);
+}
+
+template <bool F32S>
+static void col_any(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* qt,
+                    int64_t ldq, void* st, hipStream_t stream) {
+  if (dtype == 1) {
+    if (fmt == 0) col_dispatch<uint16_t, 0, F32S>(x, rows, cols, ldx, qt, ldq, st, stream);
+    else col_dispatch<uint16_t, 1, F32S>(x, rows, cols, ldx, qt, ldq, st, stream);
+  } else {
+    if (fmt == 0) col_dispatch<float, 0, F32S>(x, rows, cols, ldx, qt, ldq, st, stream);
+    else col_dispatch<float, 1, F32S>(x, rows, cols, ldx, qt, ldq, st, stream);
+  }
 }
 
 void launch_quant_col_t(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                         uint8_t* qt, int64_t ldq, uint8_t* st, hipStream_t stream) {
-  if (dtype == 1) {
-    if (fmt == 0) col_dispatch<uint16_t, 0>(x, rows, cols, ldx, qt, ldq, st, stream);
-    else col_dispatch<uint16_t, 1>(x, rows, cols, ldx, qt, ldq, st, stream);
-  } else {
-    if (fmt == 0) col_dispatch<float, 0>(x, rows, cols, ldx, qt, ldq, st, stream);
-    else col_dispatch<float, 1>(x, rows, cols, ldx, qt, ldq, st, stream);
-  }
+  col_any<false>(x, dtype, rows, cols, ldx, fmt, qt, ldq, st, stream);
+}
+
+void launch_quant_col_t_f32s(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                             uint8_t* qt, int64_t ldq, float* st, hipStream_t stream) {
+  col_any<true>(x, dtype, rows, cols, ldx, fmt, qt, ldq, st, stream);
 }
 
 template <typename InT, int FMT>
@@ -542,24 +604,35 @@ void launch_quant_block_dual(const void* w, int dtype, int64_t rows, int64_t col
   }
 }
 
-template <typename InT, int FMT>
+template <typename InT, int FMT, bool F32S>
 static void block_dispatch(const void* w, int64_t rows, int64_t cols, int64_t ldw, uint8_t* q,
-                           int64_t ldq, uint8_t* s, hipStream_t stream) {
+                           int64_t ldq, void* s, hipStream_t stream) {
   const uint32_t nbc = (uint32_t)((cols + 127) / 128);
   const dim3 grid(nbc, (uint32_t)((rows + 127) / 128));
-  hipLaunchKernelGGL((quant_block_kernel<InT, FMT>), grid, dim3(kThreads), 0, stream, (const InT*)w,
+  hipLaunchKernelGGL((quant_block_kernel<InT, FMT, F32S>), grid, dim3(kThreads), 0, stream, (const InT*)w,
                      (uint32_t)rows, (uint32_t)cols, ldw, q, ldq, s, nbc);
+}
+
+template <bool F32S>
+static void block_any(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw, int fmt, uint8_t* q,
+                      int64_t ldq, void* s, hipStream_t stream) {
+  if (dtype == 1) {
+    if (fmt == 0) block_dispatch<uint16_t, 0, F32S>(w, rows, cols, ldw, q, ldq, s, stream);
+    else block_dispatch<uint16_t, 1, F32S>(w, rows, cols, ldw, q, ldq, s, stream);
+  } else {
+    if (fmt == 0) block_dispatch<float, 0, F32S>(w, rows, cols, ldw, q, ldq, s, stream);
+    else block_dispatch<float, 1, F32S>(w, rows, cols, ldw, q, ldq, s, stream);
+  }
 }
 
 void launch_quant_block(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw, int fmt,
                         uint8_t* q, int64_t ldq, uint8_t* s, hipStream_t stream) {
-  if (dtype == 1) {
-    if (fmt == 0) block_dispatch<uint16_t, 0>(w, rows, cols, ldw, q, ldq, s, stream);
-    else block_dispatch<uint16_t, 1>(w, rows, cols, ldw, q, ldq, s, stream);
-  } else {
-    if (fmt == 0) block_dispatch<float, 0>(w, rows, cols, ldw, q, ldq, s, stream);
-    else block_dispatch<float, 1>(w, rows, cols, ldw, q, ldq, s, stream);
-  }
+  block_any<false>(w, dtype, rows, cols, ldw, fmt, q, ldq, s, stream);
+}
+
+void launch_quant_block_f32s(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw, int fmt,
+                             uint8_t* q, int64_t ldq, float* s, hipStream_t stream) {
+  block_any<true>(w, dtype, rows, cols, ldw, fmt, q, ldq, s, stream);
 }
 
 template <typename InT, int FMT, int RULE, bool COUNTS>

@@ -27,6 +27,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"fp8_quantize_token", "fp8_quantize_block", "mx_quantize", "fp8_block_scaled_gemm",
                           "mx_gemm", "fp8_quantize_token_dual", "fp8_quantize_block_dual",
+                          "fp8_quantize_token_f32s", "fp8_quantize_block_f32s", "fp8_gemm_f32s",
                           "mxfp8_status_string", "mxfp8_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -72,6 +73,32 @@ def test_block_validation():
     assert blk(ldw=16) == LD and blk(ldq=520) == LD
     assert blk(w=MIS) == ALIGN
     assert blk(q=X) == ALIAS
+
+
+def test_f32s_validation():
+    def tok(x=X, dt=1, rows=256, cols=512, ldx=512, axis=0, fmt=0, q=Q, ldq=512, s=S):
+        return mx.fp8_quantize_token_f32s(x, dt, rows, cols, ldx, axis, fmt, q, ldq, s, None)
+
+    def blk(w=X, dt=0, rows=256, cols=512, ldw=512, fmt=1, q=Q, ldq=512, s=S):
+        return mx.fp8_quantize_block_f32s(w, dt, rows, cols, ldw, fmt, q, ldq, s, None)
+
+    def g(M=256, N=256, K=512, a=X, lda=512, afmt=0, sa=S, b=Q, ldb=512, bfmt=0, blay=0, sb=P2, bsm=0, c=C,
+          ldc=256, cdt=0):
+        return mx.fp8_gemm_f32s(M, N, K, a, lda, afmt, sa, b, ldb, bfmt, blay, sb, bsm, c, ldc, cdt, None)
+    assert tok(axis=3) == ENUM and tok(fmt=2) == ENUM and tok(dt=2) == ENUM
+    assert tok(rows=-1) == SHAPE and tok(cols=520, ldx=528, ldq=528) == SHAPE
+    assert tok(axis=1, rows=136, cols=512, ldx=512, ldq=144) == SHAPE
+    assert tok(s=None) == NULL and tok(ldq=500) == LD and tok(x=MIS) == ALIGN and tok(s=S + 2) == ALIGN
+    assert tok(q=X) == ALIAS and tok(rows=0) == OK
+    assert blk(fmt=5) == ENUM and blk(cols=24, ldw=32, ldq=32) == SHAPE and blk(w=None) == NULL
+    assert blk(s=S + 1) == ALIGN and blk(s=X) == ALIAS and blk(cols=0) == OK
+    assert g(afmt=2) == ENUM and g(blay=2) == ENUM and g(bsm=2) == ENUM and g(cdt=2) == ENUM
+    assert g(blay=1, bsm=1, ldb=256) == ENUM
+    assert g(K=200) == SHAPE and g(M=-1) == SHAPE and g(M=0) == OK and g(N=0, c=None) == OK
+    assert g(c=None) == NULL and g(sa=None) == NULL and g(sb=None) == NULL
+    assert g(lda=256) == LD and g(ldb=500) == LD and g(ldc=200) == LD and g(blay=1, ldb=128) == LD
+    assert g(a=MIS) == ALIGN and g(c=MIS) == ALIGN and g(sa=S + 2) == ALIGN and g(sb=P2 + 3) == ALIGN
+    assert g(c=X) == ALIAS and g(c=S) == ALIAS and g(c=P2) == ALIAS
 
 
 Q2, S2 = 0x600000, 0x700000
