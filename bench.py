@@ -15,7 +15,8 @@ one (the GEMM) is reported against the dense FP8 MFMA peak.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 
 Other workloads (--workload): dgrad7b, wgrad, mxfprop1p5b (the fprop step on
-MX operands: 32-element E8M0 scales for X and W, mx_gemm), dualq (the
+MX operands: 32-element E8M0 scales for X and W, mx_gemm), f32sfprop1p5b
+(the fprop step with fp32 instead of power-of-two scales), dualq (the
 two-orientation quantizers on the wgrad activation and the dgrad weight),
 mxstress -- for the per-kernel roofline figures; they print the same kind of
 JSON line.
@@ -41,7 +42,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="fprop1p5b",
-                   choices=["fprop1p5b", "dgrad7b", "wgrad", "mxfprop1p5b", "dualq", "mxstress", "copy"])
+                   choices=["fprop1p5b", "dgrad7b", "wgrad", "mxfprop1p5b", "f32sfprop1p5b", "dualq", "mxstress",
+                            "copy"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=0,
                    help="token rows in the oracle sample (0 = all rows: the full step)")
@@ -351,6 +353,32 @@ def bench_other(args):
         flops = 2.0 * M * N * K
         desc = "mxfprop1p5b: MX-quantize X 4096x1536 and W 8960x1536 bf16 (32-element E4M3 blocks, OCP floor " \
                "scales) + MX GEMM M=4096 N=8960 K=1536 bf16 out"
+    elif args.workload == "f32sfprop1p5b":
+        d = synth.fprop1p5b()
+        x, w = to_dev(d["x"]), to_dev(d["w"])
+        del d
+        M, K = x.shape
+        N = w.shape[0]
+        f32 = dict(dtype=torch.float32, device="cuda")
+        xq, xs = torch.empty((M, K), **u8), torch.empty((M, K // 128), **f32)
+        wq, ws = torch.empty((N, K), **u8), torch.empty(((N + 127) // 128, K // 128), **f32)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+        def step(timer):
+            stream = cur()
+            _check(timer.run("quant_token_x_f32s", lambda: mx.fp8_quantize_token_f32s(
+                x.data_ptr(), mx.BF16, M, K, K, mx.ROW, mx.E4M3, xq.data_ptr(), K, xs.data_ptr(), stream)), "q")
+            _check(timer.run("quant_block_w_f32s", lambda: mx.fp8_quantize_block_f32s(
+                w.data_ptr(), mx.BF16, N, K, K, mx.E4M3, wq.data_ptr(), K, ws.data_ptr(), stream)), "q")
+            _check(timer.run("gemm", lambda: mx.fp8_gemm_f32s(
+                M, N, K, xq.data_ptr(), K, mx.E4M3, xs.data_ptr(), wq.data_ptr(), K, mx.E4M3, mx.B_NK,
+                ws.data_ptr(), mx.SCALE_BLOCK128, y.data_ptr(), N, mx.BF16, stream)), "gemm")
+        sizes = {"quant_token_x_f32s": M * K * 3 + 4 * M * (K // 128),
+                 "quant_block_w_f32s": N * K * 3 + 4 * ((N + 127) // 128) * (K // 128)}
+        outputs = [xq, xs, wq, ws, y]
+        flops = 2.0 * M * N * K
+        desc = "f32sfprop1p5b: token-quantize X 4096x1536 and block-quantize W 8960x1536 bf16 with fp32 scales " \
+               "(amax / 448) + GEMM over fp32-scaled operands M=4096 N=8960 K=1536 bf16 out"
     elif args.workload == "dualq":
         x = to_dev(synth.wgrad()["x"])
         w = to_dev(synth.dgrad7b(rows=16)["w"])
