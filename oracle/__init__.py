@@ -83,6 +83,15 @@ def _load():
         lib.orc_mx_gemm.restype = None
         lib.orc_mx_gemm_elems.argtypes = [I64, I64, I64, P, I64, I, P, P, I64, I, P, P, P, I64, P, P]
         lib.orc_mx_gemm_elems.restype = None
+        U64 = ctypes.c_uint64
+        lib.orc_philox4x64.argtypes = [P, P, P]
+        lib.orc_philox4x64.restype = None
+        lib.orc_gaussws_r.argtypes = [ctypes.c_uint32]
+        lib.orc_gaussws_r.restype = I
+        lib.orc_gaussws_noise.argtypes = [U64, U64, I64, I64, P]
+        lib.orc_gaussws_noise.restype = None
+        lib.orc_gaussws.argtypes = [P, I, I64, I64, I64, P, U64, U64, P, I64, I64, I64]
+        lib.orc_gaussws.restype = None
         lib.orc_decode_array.argtypes = [I, P, I64, P]
         lib.orc_encode_array.argtypes = [I, P, I64, P]
         lib.orc_encode_f32_range.argtypes = [I, ctypes.c_uint32, I64, P]
@@ -444,3 +453,48 @@ def gemm_f32s_elems(a, sa, a_fmt, b, sb, b_fmt, ii, jj, b_layout=B_NK, b_scale=B
             ctypes.c_void_p(y.ctypes.data + 8 * i0), ctypes.c_void_p(t.ctypes.data + 8 * i0))
     _run([job(i0, i1) for i0, i1 in _split(n, threads)])
     return y, t
+
+
+# ------------------------------------------------------------------------- GaussWS
+
+def philox4x64(ctr, key):
+    """Philox4x64-10 of a 4-word counter and a 2-word key: four uint64."""
+    lib = _load()
+    c = np.ascontiguousarray(ctr, dtype=np.uint64)
+    k = np.ascontiguousarray(key, dtype=np.uint64)
+    out = np.empty(4, np.uint64)
+    lib.orc_philox4x64(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def gaussws_r(u):
+    """R in {-2..2} from 32 uniform bits."""
+    return _load().orc_gaussws_r(int(u) & 0xFFFFFFFF)
+
+
+def gaussws_noise(seed, stream, rows, cols):
+    """R of every element of a [rows][cols] tensor (int8)."""
+    lib = _load()
+    out = np.empty((rows, cols), np.int8)
+    lib.orc_gaussws_noise(seed, stream, rows, cols, _ptr(out))
+    return out
+
+
+def gaussws(w, bt, seed, stream, threads=1):
+    """GaussWS sampled weight: bf16 bit patterns (uint16) [rows][cols] of
+    w + R * max_bl|w| * 2^(1 - b_t); bt int8 [ceil(rows/32)][ceil(cols/32)]."""
+    lib = _load()
+    w = np.ascontiguousarray(w)
+    dt, es = _dtype_code(w)
+    rows, cols = w.shape
+    bt = np.ascontiguousarray(bt, dtype=np.int8)
+    nbr, nbc = -(-rows // 32), -(-cols // 32)
+    if bt.shape != (nbr, nbc):
+        raise ValueError("bitwidths must be [ceil(rows/32)][ceil(cols/32)]")
+    out = np.empty((rows, cols), np.uint16)
+
+    def job(i0, i1):
+        return lambda: lib.orc_gaussws(_ptr(w), dt, rows, cols, cols, _ptr(bt), seed, stream, _ptr(out), cols,
+                                       i0, i1)
+    _run([job(a, b) for a, b in _split(nbr, threads)])
+    return out

@@ -366,6 +366,99 @@ void orc_quantize_block_f32s(const void* w, int dtype, int64_t rows, int64_t col
 }
 
 /* ---------------------------------------------------------------------- */
+/* GaussWS fake quantization (R9)                                          */
+/* ---------------------------------------------------------------------- */
+
+/* Philox4x64-10: ten rounds of two 64x64 -> 128-bit products with the
+ * published multipliers, the key bumped by the published Weyl increments
+ * after each round. */
+void orc_philox4x64(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+  uint64_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3], k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    const unsigned __int128 p0 = (unsigned __int128)M0 * x0, p1 = (unsigned __int128)M1 * x2;
+    const uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+    const uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+    x0 = hi1 ^ x1 ^ k0;
+    x1 = lo1;
+    x2 = hi0 ^ x3 ^ k1;
+    x3 = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+  out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+/* R from 32 uniform bits (R9): thresholds on the low 31 bits at
+ * P(|Z| < 1) = erf(1/sqrt 2) and P(|Z| < 3) = erf(3/sqrt 2) of a standard
+ * normal Z, times 2^31 and rounded to the nearest integer (computed once
+ * when the library is loaded). */
+static uint32_t g_r_t0, g_r_t1;
+__attribute__((constructor)) static void init_gaussws_thresholds(void) {
+  const double two31 = 2147483648.0;
+  g_r_t0 = (uint32_t)floor(erf(1.0 / sqrt(2.0)) * two31 + 0.5);
+  g_r_t1 = (uint32_t)floor(erf(3.0 / sqrt(2.0)) * two31 + 0.5);
+}
+
+int orc_gaussws_r(uint32_t u) {
+  const uint32_t m = u & 0x7FFFFFFFu;
+  const int mag = m < g_r_t0 ? 0 : (m < g_r_t1 ? 1 : 2);
+  return (u >> 31) ? -mag : mag;
+}
+
+/* The 32 uniform bits of element (r, c). */
+static uint32_t gaussws_bits(uint64_t seed, uint64_t stream, int64_t r, int64_t c) {
+  const uint64_t ctr[4] = {(uint64_t)(c / 8), (uint64_t)r, 0, 0};
+  const uint64_t key[2] = {seed, stream};
+  uint64_t out[4];
+  orc_philox4x64(ctr, key, out);
+  const uint64_t w = out[(c % 8) / 2];
+  return (c % 2) ? (uint32_t)(w >> 32) : (uint32_t)w;
+}
+
+/* fp32 -> bf16 bits, round to nearest even (finite inputs; NaN kept NaN). */
+static uint16_t bf16_rne_bits(float f) {
+  uint32_t b;
+  memcpy(&b, &f, sizeof b);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x40);
+  const uint32_t lsb = (b >> 16) & 1u;
+  return (uint16_t)((b + 0x7FFFu + lsb) >> 16);
+}
+
+/* R for every element of a [rows][cols] tensor (int8, for the tests). */
+void orc_gaussws_noise(uint64_t seed, uint64_t stream, int64_t rows, int64_t cols, int8_t* r_out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) r_out[r * cols + c] = (int8_t)orc_gaussws_r(gaussws_bits(seed, stream, r, c));
+}
+
+/* w_hat[r][c] (bf16 bits) = bf16(fp32(w + R * ldexp(max_bl |w|, 1 - b_t))),
+ * blocks of 32x32 (partial at the edges), b_t[ceil(rows/32)][ceil(cols/32)];
+ * for the block rows [i0, i1) (rows keep their index in the whole tensor). */
+void orc_gaussws(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw, const int8_t* bt,
+                 uint64_t seed, uint64_t stream, uint16_t* out, int64_t ldo, int64_t i0, int64_t i1) {
+  const int64_t G = 32, nbc = ceil_div(cols, G);
+  for (int64_t i = i0; i < i1; ++i)
+    for (int64_t j = 0; j < nbc; ++j) {
+      const int64_t r0 = i * G, r1 = min64(r0 + G, rows);
+      const int64_t c0 = j * G, c1 = min64(c0 + G, cols);
+      double amax = 0.0;
+      for (int64_t r = r0; r < r1; ++r)
+        for (int64_t c = c0; c < c1; ++c) {
+          const double a = fabs(load_elem(w, dtype, r * ldw + c));
+          if (a > amax) amax = a;
+        }
+      const float scale = ldexpf((float)amax, 1 - (int)bt[i * nbc + j]);
+      for (int64_t r = r0; r < r1; ++r)
+        for (int64_t c = c0; c < c1; ++c) {
+          const float noise = (float)orc_gaussws_r(gaussws_bits(seed, stream, r, c)) * scale;
+          const float v = (float)load_elem(w, dtype, r * ldw + c) + noise;
+          out[r * ldo + c] = bf16_rne_bits(v);
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------- */
 /* Block-scaled GEMM [INFR "What carries the argument"; R7]                */
 /* ---------------------------------------------------------------------- */
 

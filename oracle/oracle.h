@@ -79,6 +79,12 @@ void orc_mx_gemm_elems(int64_t M, int64_t N, int64_t K,
                        const uint8_t* b, int64_t ldb, int b_fmt, const uint8_t* sb,
                        const int64_t* ii, const int64_t* jj, int64_t n, double* y, double* t);
 
+void orc_philox4x64(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]);
+int orc_gaussws_r(uint32_t u);
+void orc_gaussws_noise(uint64_t seed, uint64_t stream, int64_t rows, int64_t cols, int8_t* r_out);
+void orc_gaussws(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw, const int8_t* bt,
+                 uint64_t seed, uint64_t stream, uint16_t* out, int64_t ldo, int64_t i0, int64_t i1);
+
 void orc_decode_array(int fmt, const uint8_t* codes, int64_t n, double* out);
 void orc_encode_array(int fmt, const double* x, int64_t n, uint8_t* out);
 void orc_encode_f32_range(int fmt, uint32_t start, int64_t n, uint8_t* out);
