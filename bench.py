@@ -18,6 +18,7 @@ Other workloads (--workload): dgrad7b, wgrad, mxfprop1p5b (the fprop step on
 MX operands: 32-element E8M0 scales for X and W, mx_gemm), f32sfprop1p5b
 (the fprop step with fp32 instead of power-of-two scales), dualq (the
 two-orientation quantizers on the wgrad activation and the dgrad weight),
+gaussws7b (GaussWS sampling of the dgrad weight from fp32 master weights),
 mxstress -- for the per-kernel roofline figures; they print the same kind of
 JSON line.
 
@@ -42,8 +43,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="fprop1p5b",
-                   choices=["fprop1p5b", "dgrad7b", "wgrad", "mxfprop1p5b", "f32sfprop1p5b", "dualq", "mxstress",
-                            "copy"])
+                   choices=["fprop1p5b", "dgrad7b", "wgrad", "mxfprop1p5b", "f32sfprop1p5b", "dualq", "gaussws7b",
+                            "mxstress", "copy"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=0,
                    help="token rows in the oracle sample (0 = all rows: the full step)")
@@ -379,6 +380,26 @@ def bench_other(args):
         flops = 2.0 * M * N * K
         desc = "f32sfprop1p5b: token-quantize X 4096x1536 and block-quantize W 8960x1536 bf16 with fp32 scales " \
                "(amax / 448) + GEMM over fp32-scaled operands M=4096 N=8960 K=1536 bf16 out"
+    elif args.workload == "gaussws7b":
+        wf = synth.bf16_bits_to_f32(synth.dgrad7b(rows=16)["w"]).astype(np.float32)
+        R, C = wf.shape
+        bt_np = np.random.default_rng(10).integers(4, 9, (-(-R // 32), -(-C // 32))).astype(np.int8)
+        w = to_dev(wf)
+        bt = torch.from_numpy(bt_np).cuda()
+        del wf
+        w_hat = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+        counter = [0]
+
+        def step(timer):
+            stream = cur()
+            _check(timer.run("gaussws", lambda: mx.gaussws_sample(
+                w.data_ptr(), mx.F32, R, C, C, bt.data_ptr(), 2025, 7, w_hat.data_ptr(), C, stream)), "gws")
+        sizes = {"gaussws": R * C * 6 + bt_np.size}
+        outputs = [w_hat]
+        flops = 0.0
+        M = N = K = 0
+        desc = "gaussws7b: GaussWS sampled weight of W 18944x3584 fp32 master weights (32x32 blocks, int8 " \
+               "bitwidths 4..8, Philox4x64-10 rounded-normal noise) -> bf16"
     elif args.workload == "dualq":
         x = to_dev(synth.wgrad()["x"])
         w = to_dev(synth.dgrad7b(rows=16)["w"])

@@ -18,6 +18,11 @@
  *          and Fig. 5: 32-element MX blocks sharing one E8M0 scale, the
  *          clamping of scaled values above the largest code, and a monitor
  *          of the clamped fraction ("Reading between the lines").
+ *   [GWS]  "Gaussian Weight Sampling for Scalable, Efficient and Stable
+ *          Pseudo-Quantization Training", review page, "The reading" and
+ *          "What carries the argument": the sampled weight
+ *          w + R * max_bl(|w|) * 2^(1 - b_t) with rounded-normal R and a
+ *          bitwidth b_t per 32x32 block, cast to BF16.
  *
  * Conventions shared by every entry point
  *   - Pointers to tensors are DEVICE pointers owned by the caller; the
@@ -266,6 +271,32 @@ int fp8_gemm_f32s(int64_t M, int64_t N, int64_t K,
 int mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, int a_fmt,
             const uint8_t* a_scales, const uint8_t* b, int64_t ldb, int b_fmt, const uint8_t* b_scales,
             void* c, int64_t ldc, int c_dtype, void* stream);
+
+/*
+ * gaussws_sample -- GaussWS sampled weight [GWS "What carries the argument"]:
+ *
+ *   w_hat[r][c] = bf16( fp32( w[r][c] + R(r, c) * ldexp(amax_bl, 1 - b_bl) ) )
+ *
+ * over 32x32 blocks bl (partial at the edges), amax_bl = max |w| in the
+ * block, b_bl = bitwidths[r / 32][c / 32] (int8, read as an integer
+ * exponent), R the nearest integer to N(0,1)/2 with support folded to
+ * {-2..2}: |R| = 0, 1, 2 as |Z| < 1, 1 <= |Z| < 3, |Z| >= 3 (P(R = 0) =
+ * 0.6827).  The page's bitwise approximation of R is not printed; R is drawn
+ * here by its definition from 32 uniform bits per element: bit 31 the sign,
+ * bits 0..30 against round(erf(1/sqrt 2) * 2^31) and round(erf(3/sqrt 2) *
+ * 2^31).  The bits are the counter-based Philox4x64-10 (Salmon et al.,
+ * SC'11) with key (seed, stream_id) and counter (c / 8, r, 0, 0): output
+ * word (c % 8) / 2, low half for even c, high half for odd c.  The result
+ * depends only on (seed, stream_id, r, c) and the inputs, so it is
+ * deterministic and reproducible across calls and launch shapes.
+ *   w:         [rows][ldw >= cols] fp32 or bf16 (w_dtype).
+ *   bitwidths: [ceil(rows / 32)][ceil(cols / 32)] int8.
+ *   w_hat:     [rows][ldo >= cols] bf16 bit patterns, overwritten.
+ * Requires cols % 8 == 0.  The fp32 sum is rounded to bf16 to nearest even.
+ */
+int gaussws_sample(const void* w, int w_dtype, int64_t rows, int64_t cols, int64_t ldw,
+                   const int8_t* bitwidths, uint64_t seed, uint64_t stream_id, uint16_t* w_hat,
+                   int64_t ldo, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* mxfp8_status_string(int status);

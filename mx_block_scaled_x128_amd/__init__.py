@@ -9,12 +9,12 @@ entry point raises -- there is no fallback path.
 Low-level entry points carry the C names and signatures (pointers as ints):
   fp8_quantize_token, fp8_quantize_block, fp8_quantize_token_dual,
   fp8_quantize_block_dual, fp8_quantize_token_f32s, fp8_quantize_block_f32s,
-  mx_quantize, fp8_block_scaled_gemm, fp8_gemm_f32s, mx_gemm,
+  mx_quantize, fp8_block_scaled_gemm, fp8_gemm_f32s, mx_gemm, gaussws_sample,
   mxfp8_status_string, mxfp8_version.
 Tensor conveniences allocate outputs with torch and call them:
   quantize_token, quantize_block, quantize_token_dual, quantize_block_dual,
   quantize_token_f32s, quantize_block_f32s, quantize_mx, block_scaled_gemm,
-  gemm_f32s, mx_scaled_gemm.
+  gemm_f32s, mx_scaled_gemm, gaussws.
 """
 import ctypes
 import os
@@ -25,10 +25,10 @@ __all__ = [
     "SCALE_BLOCK128", "SCALE_ROW128", "MxFp8Error", "library_path", "load_library",
     "fp8_quantize_token", "fp8_quantize_block", "fp8_quantize_token_dual", "fp8_quantize_block_dual",
     "fp8_quantize_token_f32s", "fp8_quantize_block_f32s", "mx_quantize", "fp8_block_scaled_gemm",
-    "fp8_gemm_f32s", "mx_gemm", "mxfp8_status_string", "mxfp8_version",
+    "fp8_gemm_f32s", "mx_gemm", "gaussws_sample", "mxfp8_status_string", "mxfp8_version",
     "quantize_token", "quantize_block", "quantize_token_dual", "quantize_block_dual",
     "quantize_token_f32s", "quantize_block_f32s", "quantize_mx", "block_scaled_gemm", "gemm_f32s",
-    "mx_scaled_gemm",
+    "mx_scaled_gemm", "gaussws",
 ]
 
 # enum values of include/mxfp8.h
@@ -86,6 +86,8 @@ def load_library():
         lib.fp8_gemm_f32s.restype = I
         lib.mx_gemm.argtypes = [I64, I64, I64, P, I64, I, P, P, I64, I, P, P, I64, I, P]
         lib.mx_gemm.restype = I
+        lib.gaussws_sample.argtypes = [P, I, I64, I64, I64, P, ctypes.c_uint64, ctypes.c_uint64, P, I64, P]
+        lib.gaussws_sample.restype = I
         lib.mxfp8_status_string.argtypes = [I]
         lib.mxfp8_status_string.restype = ctypes.c_char_p
         lib.mxfp8_version.argtypes = []
@@ -142,6 +144,11 @@ def fp8_gemm_f32s(M, N, K, a, lda, a_fmt, a_scales, b, ldb, b_fmt, b_layout, b_s
 def mx_gemm(M, N, K, a, lda, a_fmt, a_scales, b, ldb, b_fmt, b_scales, c, ldc, c_dtype, stream):
     return load_library().mx_gemm(M, N, K, a, lda, a_fmt, a_scales, b, ldb, b_fmt, b_scales, c, ldc, c_dtype,
                                   stream)
+
+
+def gaussws_sample(w, w_dtype, rows, cols, ldw, bitwidths, seed, stream_id, w_hat, ldo, stream):
+    return load_library().gaussws_sample(w, w_dtype, rows, cols, ldw, bitwidths, seed, stream_id, w_hat, ldo,
+                                         stream)
 
 
 def mxfp8_status_string(status):
@@ -344,4 +351,17 @@ def gemm_f32s(a, a_scales, a_fmt, b, b_scales, b_fmt, b_layout=B_NK, b_scale_mod
                        b_layout, b_scales.data_ptr(), b_scale_mode, out.data_ptr(), _ld(out), c_dtype,
                        _stream(stream))
     _check(st, "fp8_gemm_f32s")
+    return out
+
+
+def gaussws(w, bitwidths, seed, stream_id=0, out=None, stream=None):
+    """GaussWS sampled weight (bf16 tensor) of w with int8 bitwidths per 32x32 block."""
+    torch = _torch()
+    rows, cols = w.shape
+    if out is None:
+        buf = torch.empty((rows, _pad16(max(cols, 1))), dtype=torch.bfloat16, device=w.device)
+        out = buf[:, :cols]
+    st = gaussws_sample(w.data_ptr(), _in_dtype(w), rows, cols, _ld(w), bitwidths.data_ptr(), seed, stream_id,
+                        out.data_ptr(), _ld(out), _stream(stream))
+    _check(st, "gaussws_sample")
     return out

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxfp8.so")
-SOURCES = ["api.cpp", "quant.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "quant.hip", "gemm.hip", "gaussws.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

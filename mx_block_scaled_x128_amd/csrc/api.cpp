@@ -238,6 +238,23 @@ int mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, int 
   return launch_status();
 }
 
+int gaussws_sample(const void* w, int w_dtype, int64_t rows, int64_t cols, int64_t ldw, const int8_t* bitwidths,
+                   uint64_t seed, uint64_t stream_id, uint16_t* w_hat, int64_t ldo, void* stream) {
+  if (w_dtype != MXFP8_F32 && w_dtype != MXFP8_BF16) return MXFP8_ERR_ENUM;
+  if (rows < 0 || cols < 0) return MXFP8_ERR_SHAPE;
+  if (rows > INT32_MAX / 2 || cols > INT32_MAX / 2) return MXFP8_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return MXFP8_OK;
+  if (!w || !bitwidths || !w_hat) return MXFP8_ERR_NULL;
+  if (ldw < cols || ldw % 16 != 0) return MXFP8_ERR_LD;
+  if (ldo < cols || ldo % 16 != 0) return MXFP8_ERR_LD;
+  if (cols % 8 != 0) return MXFP8_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(w_hat)) return MXFP8_ERR_ALIGN;
+  if ((const void*)w_hat == w || (const void*)w_hat == (const void*)bitwidths) return MXFP8_ERR_ALIAS;
+  (void)hipGetLastError();
+  mxfp8::launch_gaussws(w, w_dtype, rows, cols, ldw, bitwidths, seed, stream_id, w_hat, ldo, (hipStream_t)stream);
+  return launch_status();
+}
+
 const char* mxfp8_status_string(int status) {
   switch (status) {
     case MXFP8_OK: return "ok";

@@ -53,4 +53,9 @@ void launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t l
                     const uint8_t* sa, const uint8_t* b, int64_t ldb, int b_fmt, const uint8_t* sb, void* c,
                     int64_t ldc, int c_dtype, hipStream_t stream);
 
+// GaussWS sampled weight (bf16 bits): 32x32 blocks, int8 bitwidth per block.
+// cols % 8 == 0.
+void launch_gaussws(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw, const int8_t* bt,
+                    uint64_t seed, uint64_t stream_id, uint16_t* out, int64_t ldo, hipStream_t stream);
+
 }  // namespace mxfp8

@@ -28,6 +28,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) >= {"fp8_quantize_token", "fp8_quantize_block", "mx_quantize", "fp8_block_scaled_gemm",
                           "mx_gemm", "fp8_quantize_token_dual", "fp8_quantize_block_dual",
                           "fp8_quantize_token_f32s", "fp8_quantize_block_f32s", "fp8_gemm_f32s",
+                          "gaussws_sample",
                           "mxfp8_status_string", "mxfp8_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -99,6 +100,18 @@ def test_f32s_validation():
     assert g(lda=256) == LD and g(ldb=500) == LD and g(ldc=200) == LD and g(blay=1, ldb=128) == LD
     assert g(a=MIS) == ALIGN and g(c=MIS) == ALIGN and g(sa=S + 2) == ALIGN and g(sb=P2 + 3) == ALIGN
     assert g(c=X) == ALIAS and g(c=S) == ALIAS and g(c=P2) == ALIAS
+
+
+def test_gaussws_validation():
+    def call(w=X, dt=0, rows=64, cols=256, ldw=256, bt=S, out=Q, ldo=256):
+        return mx.gaussws_sample(w, dt, rows, cols, ldw, bt, 1, 2, out, ldo, None)
+    assert call(dt=2) == ENUM
+    assert call(rows=-1) == SHAPE and call(cols=250, ldw=256, ldo=256) == SHAPE and call(rows=2 ** 31) == SHAPE
+    assert call(rows=0, w=None, bt=None, out=None) == OK and call(cols=0) == OK
+    assert call(w=None) == NULL and call(bt=None) == NULL and call(out=None) == NULL
+    assert call(ldw=240) == LD and call(ldw=264) == LD and call(ldo=250) == LD
+    assert call(w=MIS) == ALIGN and call(out=MIS) == ALIGN
+    assert call(out=X) == ALIAS and call(out=S) == ALIAS
 
 
 Q2, S2 = 0x600000, 0x700000
