@@ -45,6 +45,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
@@ -622,7 +623,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // Stored from registers directly, that is 16 rows x 16 bytes per store
   // instruction.  Instead each wave stages one 32-row strip of its
   // sub-tile at a time in LDS and writes it back row by row: every store
-  // instruction then covers whole 256-byte row segments.  The staging sits
+  // instruction then covers whole 256-byte row segments.  The stores are
+  // non-temporal: output lines are written once, and kept out of L2 they
+  // leave the operand tiles other workgroups still read in place (measured:
+  // 5 % on the fprop shape, none lost elsewhere).  The staging sits
   // in two ring slots nothing reads any more (waves 0, 1 in the first, 2, 3
   // in the second); only the wave itself touches its region, and LDS
   // executes one wave's accesses in order, so no barrier is needed.
@@ -653,7 +657,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
           if (m < M) {
             float* dst = reinterpret_cast<float*>(C) + (int64_t)m * ldc + n;
             if (n + 3 < N) {
-              *reinterpret_cast<v4f*>(dst) = v;
+              __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(dst));
             } else {
 #pragma unroll
               for (int i = 0; i < 4; ++i)
@@ -688,7 +692,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
           if (m < M) {
             uint16_t* dst = reinterpret_cast<uint16_t*>(C) + (int64_t)m * ldc + n;
             if (n + 7 < N) {
-              *reinterpret_cast<uint4*>(dst) = v;
+              __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
             } else {
               const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
