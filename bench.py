@@ -82,6 +82,70 @@ class KernelTimer:
     def mean(self, name):
         return float(np.mean(self.times[name]))
 
+    def median(self, name):
+        return float(np.median(self.times[name]))
+
+
+class ColdTimer(KernelTimer):
+    """Like KernelTimer, but every timed call is preceded by a write of a 512 MiB scrub
+    buffer (twice the 256 MB last-level cache), outside the event pair: the call then
+    finds none of its inputs in the caches."""
+
+    def __init__(self, scrub):
+        super().__init__()
+        self.scrub = scrub
+        self.count = 0
+
+    def run(self, name, fn):
+        self.count += 1
+        self.scrub.fill_(self.count & 0xFF)
+        return super().run(name, fn)
+
+
+def context_measurements(step, timer, reps=10):
+    """Median warm and cold (scrubbed) per-call times, the device description and a
+    measured device copy bandwidth, added to the JSON line as context."""
+    import torch
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = ColdTimer(scrub)
+    step(cold)  # warm-up of the scrub path
+    torch.cuda.synchronize()
+    cold.pending = []
+    for _ in range(reps):
+        step(cold)
+    torch.cuda.synchronize()
+    cold.collect()
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * 10 / (s.elapsed_time(e) * 1e-3) / 1e9
+    del scrub, src, dst
+    props = torch.cuda.get_device_properties(0)
+    per = {name: {"us_median": round(timer.median(name) * 1e6, 2),
+                  "us_cold_median": round(cold.median(name) * 1e6, 2)} for name in timer.times}
+    return per, {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                 "compute_units": props.multi_processor_count, "copy_256MiB_GBs": round(copy_gbs, 1)}
+
+
+def add_context(line, step, timer):
+    per, device = context_measurements(step, timer)
+    for name, d in per.items():
+        if name in line["kernels"]:
+            line["kernels"][name].update(d)
+    line["device"] = device
+    line["timing"] = ("value: graph replays of the whole step between synchronisations; kernels.us: mean of "
+                      "event-bracketed eager calls (us_median: median); us_cold_median: each call after a "
+                      "512 MiB scrub write, medians of 10")
+    return line
+
 
 class _NoTimer:
     def run(self, name, fn):
@@ -248,6 +312,7 @@ def bench_fprop(args):
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None},
     }
+    add_context(line, step, timer)
     line["cpu_baseline"] = None if args.no_cpu else cpu_baseline_fprop(t["host"], args.cpu_rows)
     return line
 
@@ -460,7 +525,7 @@ def bench_other(args):
         dom = max(sizes, key=lambda k: kern[k]["us"])
         roof = {"bound": "hbm", "achieved": kern[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": kern[dom]["frac_hbm_peak"], "traffic": None, "kernel": dom}
-    return {
+    line = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(per_step * 1e3, 4),
         "ms_per_step_eager": round(per_step_eager * 1e3, 4), "higher_is_better": True,
@@ -468,6 +533,9 @@ def bench_other(args):
         "config": {"workload": desc, "M": M, "N": N, "K": K}, "kernels": kern, "roofline": roof,
         "cpu_baseline": None,
     }
+    if args.workload != "mxstress":  # 64 launches per step: the scrubbed pass would take long
+        add_context(line, step, timer)
+    return line
 
 
 def main():
