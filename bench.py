@@ -269,6 +269,22 @@ def cpu_baseline_fprop(host, rows):
     }
 
 
+def gemm_traffic(workload):
+    """HBM bytes per GEMM call from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded
+    under profiles/ (scaled by a plain copy's counters), or None when the GEMM kernel's
+    source has changed since they were taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    rec_path = os.path.join(here, "profiles", "gemm_traffic_%s.json" % workload)
+    src = os.path.join(here, "mx_block_scaled_x128_amd", "csrc", "gemm.hip")
+    if not os.path.exists(rec_path):
+        return None
+    rec = json.load(open(rec_path))
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("gemm_source_sha256"):
+        return None
+    return int(rec["fetch_bytes_per_call"] + rec["write_bytes_per_call"])
+
+
 def bytes_token(rows, cols, in_bytes):
     return rows * cols * (in_bytes + 1) + rows * ((cols + 127) // 128)
 
@@ -310,7 +326,12 @@ def bench_fprop(args):
                      "frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "flops": flops},
         },
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": FP8_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
+                     "traffic": gemm_traffic("fprop1p5b"),
+                     "traffic_note": "HBM bytes per GEMM call (FETCH_SIZE + WRITE_SIZE, copy-calibrated; "
+                                     "profiles/gemm_traffic_fprop1p5b.json); algorithmic bytes %d"
+                                     % (M * K + N * K + M * (K // 128) + ((N + 127) // 128) * (K // 128)
+                                        + 2 * M * N)},
     }
     add_context(line, step, timer)
     line["cpu_baseline"] = None if args.no_cpu else cpu_baseline_fprop(t["host"], args.cpu_rows)
