@@ -1,7 +1,9 @@
 /*
  * mxfp8.h -- C ABI of libmxfp8: hybrid-granularity FP8 quantization with
  * power-of-two (E8M0) scales, and the block-scaled FP8 GEMM that consumes it,
- * for AMD Instinct MI355X (gfx950).
+ * for AMD Instinct MI355X (gfx950).  Next to them: the MX GEMM on 32-element
+ * scales, two-orientation quantizers, an fp32-scale variant of the quantizers
+ * and the GEMM, and the GaussWS weight sampler.
  *
  * Sources (web pages, cited by title and section):
  *   [FP8F] "FP8 Formats for Deep Learning", review page, "Core claim": the
@@ -33,8 +35,11 @@
  *     (no leading dimension).  A scale byte b stands for 2^(b - 127).
  *   - Inputs are never written; outputs are overwritten in full (codes
  *     beyond the logical width of a row, up to `ld`, are not touched).
- *   - Alignment: every tensor pointer is 16-byte aligned and every `ld` is a
- *     multiple of 16 elements (MXFP8_ERR_ALIGN / MXFP8_ERR_LD otherwise).
+ *   - Alignment: every code or value tensor pointer is 16-byte aligned and
+ *     every `ld` is a multiple of 16 elements (MXFP8_ERR_ALIGN /
+ *     MXFP8_ERR_LD otherwise).  Byte scale arrays need no alignment; scale
+ *     arrays read as 32-bit words (fp32 scales, mx_gemm's scales) are 4-byte
+ *     aligned.
  *   - Outputs must not share an address with an input (MXFP8_ERR_ALIAS,
  *     checked by pointer equality; partial overlap is undefined).
  *   - Empty problems (a zero extent) return MXFP8_OK without launching, and
