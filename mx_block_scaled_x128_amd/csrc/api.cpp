@@ -12,6 +12,10 @@ namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The GEMM kernels address an operand tile as a base plus 32-bit per-lane
+// offsets of up to 255 rows times the leading dimension.
+constexpr int64_t kMaxGemmLd = int64_t(1) << 24;
+
 // Shared checks for the quantizers' input / code tensors.
 int check_tensor_pair(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, const uint8_t* q,
                       int64_t ldq, int64_t q_row_len, const void* scales) {
@@ -167,6 +171,7 @@ int fp8_block_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int
     if (lda < K || lda % 16 != 0) return MXFP8_ERR_LD;
     const int64_t b_row = b_layout == MXFP8_B_NK ? K : N;
     if (ldb < b_row || ldb % 16 != 0) return MXFP8_ERR_LD;
+    if (lda > kMaxGemmLd || ldb > kMaxGemmLd) return MXFP8_ERR_LD;
     if (!aligned16(a) || !aligned16(b)) return MXFP8_ERR_ALIGN;
   }
   if (!aligned16(c)) return MXFP8_ERR_ALIGN;
@@ -198,6 +203,7 @@ int fp8_gemm_f32s(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda
     if (lda < K || lda % 16 != 0) return MXFP8_ERR_LD;
     const int64_t b_row = b_layout == MXFP8_B_NK ? K : N;
     if (ldb < b_row || ldb % 16 != 0) return MXFP8_ERR_LD;
+    if (lda > kMaxGemmLd || ldb > kMaxGemmLd) return MXFP8_ERR_LD;
     if (!aligned16(a) || !aligned16(b)) return MXFP8_ERR_ALIGN;
     if (((uintptr_t)a_scales & 3) || ((uintptr_t)b_scales & 3)) return MXFP8_ERR_ALIGN;
   }
@@ -226,6 +232,7 @@ int mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, int 
   if (K > 0) {
     if (lda < K || lda % 16 != 0) return MXFP8_ERR_LD;
     if (ldb < K || ldb % 16 != 0) return MXFP8_ERR_LD;
+    if (lda > kMaxGemmLd || ldb > kMaxGemmLd) return MXFP8_ERR_LD;
     if (!aligned16(a) || !aligned16(b)) return MXFP8_ERR_ALIGN;
     if (((uintptr_t)a_scales & 3) || ((uintptr_t)b_scales & 3)) return MXFP8_ERR_ALIGN;
   }

@@ -72,11 +72,13 @@ __global__ __launch_bounds__(kThreads) void gaussws_kernel(const InT* __restrict
                                                            uint64_t seed, uint64_t stream_id,
                                                            uint16_t* __restrict__ out, int64_t ldo) {
   const uint32_t tid = threadIdx.x;
+  const uint32_t gx = (cols + 255) >> 8;   // 1-D grid: workgroup b is strip (b % gx, b / gx)
+  const uint32_t by = blockIdx.x / gx, bx = blockIdx.x - by * gx;
   const uint32_t j = tid >> 5;             // block of the strip
   const uint32_t cc = tid & 3;             // 8-column chunk in the block
   const uint32_t rg = (tid & 31) >> 2;     // 4-row group in the block
-  const uint32_t r0 = blockIdx.y * 32 + rg * 4;
-  const uint32_t col = blockIdx.x * 256 + j * 32 + cc * 8;
+  const uint32_t r0 = by * 32 + rg * 4;
+  const uint32_t col = bx * 256 + j * 32 + cc * 8;
   const bool cact = col < cols;            // cols % 8 == 0: a chunk is wholly in or out
   float f[4][8];
 #pragma unroll
@@ -94,8 +96,8 @@ __global__ __launch_bounds__(kThreads) void gaussws_kernel(const InT* __restrict
   m = max_row16(m);
   const uint32_t o = (uint32_t)__shfl_xor((int)m, 16);
   m = m > o ? m : o;  // the 32 lanes of this block
-  const uint32_t bj = (blockIdx.x * 256 + j * 32) >> 5;
-  const int b = bj < nbc ? (int)bt[(int64_t)blockIdx.y * nbc + bj] : 0;
+  const uint32_t bj = (bx * 256 + j * 32) >> 5;
+  const int b = bj < nbc ? (int)bt[(int64_t)by * nbc + bj] : 0;
   const float scale = ldexpf(__uint_as_float(m), 1 - b);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -120,7 +122,7 @@ using namespace gaussws_detail;
 void launch_gaussws(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw, const int8_t* bt,
                     uint64_t seed, uint64_t stream_id, uint16_t* out, int64_t ldo, hipStream_t stream) {
   const uint32_t nbc = (uint32_t)((cols + 31) / 32);
-  const dim3 grid((uint32_t)((cols + 255) / 256), (uint32_t)((rows + 31) / 32));
+  const dim3 grid((uint32_t)((cols + 255) / 256) * (uint32_t)((rows + 31) / 32));
   if (dtype == 1)
     hipLaunchKernelGGL((gaussws_kernel<uint16_t>), grid, dim3(kThreads), 0, stream, (const uint16_t*)w,
                        (uint32_t)rows, (uint32_t)cols, ldw, bt, nbc, seed, stream_id, out, ldo);

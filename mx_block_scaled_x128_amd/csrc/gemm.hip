@@ -36,6 +36,8 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 namespace mxfp8 {
 
 namespace gemm_detail {
@@ -740,17 +742,18 @@ void launch_tile(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
                      c_dtype == 1 ? 1 : 0, tiles_m, tiles_n, tile_first, split);
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; concurrent first
+// calls store the same value).
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 // Tile choice: 256x256 (128x128 per wave, the lowest LDS traffic per MFMA) when

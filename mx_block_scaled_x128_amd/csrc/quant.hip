@@ -21,6 +21,16 @@ namespace quant_detail {
 constexpr int kThreads = 256;
 constexpr uint32_t kMaxBlocks = 256 * 8;  // 8 workgroups per CU, grid-stride beyond that
 
+// Tile kernels run on 1-D grids (a 2-D grid's y extent is limited to 65535):
+// workgroup b is tile (b % gx, b / gx) of a gx-wide tile grid, x fastest.
+struct TileXY {
+  uint32_t x, y;
+};
+__device__ __forceinline__ TileXY tile_xy(uint32_t gx) {
+  const uint32_t y = blockIdx.x / gx;
+  return TileXY{blockIdx.x - y * gx, y};
+}
+
 __device__ __forceinline__ void zero8(float (&f)[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) f[j] = 0.0f;
@@ -168,7 +178,8 @@ __global__ __launch_bounds__(kThreads) void quant_col_t_kernel(
   const uint32_t tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint32_t tr = (lane & 7) + 8 * (w & 1);   // token chunk: tokens tr*8 .. tr*8+7
   const uint32_t tc = (lane >> 3) + 8 * (w >> 1); // channel chunk: channels tc*8 .. tc*8+7
-  const uint32_t c0 = blockIdx.x * 128, t0 = blockIdx.y * 128;
+  const TileXY b = tile_xy((cols + 127) >> 7);
+  const uint32_t c0 = b.x * 128, t0 = b.y * 128;
   const bool cact = c0 + tc * 8 < cols;
   float f[8][8];  // [token][channel]
 #pragma unroll
@@ -195,11 +206,11 @@ __global__ __launch_bounds__(kThreads) void quant_col_t_kernel(
     if constexpr (F32S) {
       const float sf = scale_f32<FMT>(a);
       exps[tid] = __float_as_int(sf);
-      if (c0 + tid < cols) static_cast<float*>(st)[(int64_t)(c0 + tid) * ngt + blockIdx.y] = sf;
+      if (c0 + tid < cols) static_cast<float*>(st)[(int64_t)(c0 + tid) * ngt + b.y] = sf;
     } else {
       const int e = scale_exp_ceil<FMT>(a);
       exps[tid] = e;
-      if (c0 + tid < cols) static_cast<uint8_t*>(st)[(int64_t)(c0 + tid) * ngt + blockIdx.y] = (uint8_t)(e + 127);
+      if (c0 + tid < cols) static_cast<uint8_t*>(st)[(int64_t)(c0 + tid) * ngt + b.y] = (uint8_t)(e + 127);
     }
   }
   __syncthreads();
@@ -252,7 +263,8 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
   const uint32_t tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint32_t tr = (lane & 7) + 8 * (w & 1);   // token chunk: tokens tr*8 .. tr*8+7
   const uint32_t tc = (lane >> 3) + 8 * (w >> 1); // channel chunk: channels tc*8 .. tc*8+7
-  const uint32_t c0 = blockIdx.x * 128, t0 = blockIdx.y * 128;
+  const TileXY b = tile_xy(ngc);
+  const uint32_t c0 = b.x * 128, t0 = b.y * 128;
   const bool cact = c0 + tc * 8 < cols;
   float f[8][8];  // [token][channel]
 #pragma unroll
@@ -289,13 +301,13 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
     const uint32_t a = max(red[0][tid], red[1][tid]);
     const int e = scale_exp_ceil<FMT>(a);
     exps[tid] = e;
-    if (c0 + tid < cols) st[(int64_t)(c0 + tid) * ngt + blockIdx.y] = (uint8_t)(e + 127);
+    if (c0 + tid < cols) st[(int64_t)(c0 + tid) * ngt + b.y] = (uint8_t)(e + 127);
   } else {
     const uint32_t t = tid - 128;
     const uint32_t a = max(rred[0][t], rred[1][t]);
     const int e = scale_exp_ceil<FMT>(a);
     rexps[t] = e;
-    if (t0 + t < rows) s[(int64_t)(t0 + t) * ngc + blockIdx.x] = (uint8_t)(e + 127);
+    if (t0 + t < rows) s[(int64_t)(t0 + t) * ngc + b.x] = (uint8_t)(e + 127);
   }
   __syncthreads();
   // Column codes into the transposed tile; row codes into the row tile.
@@ -333,7 +345,8 @@ __global__ __launch_bounds__(kThreads) void quant_block_dual_kernel(
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t tr = (lane & 7) + 8 * (wv & 1);   // row chunk: rows tr*8 .. tr*8+7
   const uint32_t tc = (lane >> 3) + 8 * (wv >> 1); // column chunk: columns tc*8 .. tc*8+7
-  const uint32_t c0 = blockIdx.x * 128, r0 = blockIdx.y * 128;
+  const TileXY b = tile_xy(nbc);
+  const uint32_t c0 = b.x * 128, r0 = b.y * 128;
   const bool cact = c0 + tc * 8 < cols;
   float f[8][8];  // [row][column]
 #pragma unroll
@@ -364,8 +377,8 @@ __global__ __launch_bounds__(kThreads) void quant_block_dual_kernel(
   for (int i = 0; i < 8; ++i)
     *reinterpret_cast<uint2*>(rtile + row_tile_offset(tr * 8 + i, tc)) = codes8<FMT>(f[i], sc);
   if (tid == 0) {
-    s[(int64_t)blockIdx.y * nbc + blockIdx.x] = (uint8_t)(e + 127);
-    st[(int64_t)blockIdx.x * nbr + blockIdx.y] = (uint8_t)(e + 127);
+    s[(int64_t)b.y * nbc + b.x] = (uint8_t)(e + 127);
+    st[(int64_t)b.x * nbr + b.y] = (uint8_t)(e + 127);
   }
   __syncthreads();
   store_tile_t(tile, qt, ldqt, c0, r0, cols, rows, tid);
@@ -386,7 +399,8 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t tc = lane & 15;               // column chunk: columns tc*8 .. tc*8+7
   const uint32_t tr = (lane >> 4) + 4 * wv;    // row chunk: rows tr*8 .. tr*8+7
-  const uint32_t r0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
+  const TileXY b = tile_xy(nbc);
+  const uint32_t r0 = b.y * 128, c0 = b.x * 128;
   const bool cact = c0 + tc * 8 < cols;
   float f[8][8];
 #pragma unroll
@@ -411,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(
       const uint32_t r = r0 + tr * 8 + i;
       if (cact && r < rows) store_nt(q + (int64_t)r * ldq + c0 + tc * 8, codes8_div<FMT>(f[i], sf));
     }
-    if (tid == 0) static_cast<float*>(s)[(int64_t)blockIdx.y * nbc + blockIdx.x] = sf;
+    if (tid == 0) static_cast<float*>(s)[(int64_t)b.y * nbc + b.x] = sf;
   } else {
     const int e = scale_exp_ceil<FMT>(m);
     const float sc = pow2_neg(e);
@@ -420,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(
       const uint32_t r = r0 + tr * 8 + i;
       if (cact && r < rows) store_nt(q + (int64_t)r * ldq + c0 + tc * 8, codes8<FMT>(f[i], sc));
     }
-    if (tid == 0) static_cast<uint8_t*>(s)[(int64_t)blockIdx.y * nbc + blockIdx.x] = (uint8_t)(e + 127);
+    if (tid == 0) static_cast<uint8_t*>(s)[(int64_t)b.y * nbc + b.x] = (uint8_t)(e + 127);
   }
 }
 
@@ -537,7 +551,7 @@ template <typename InT, int FMT, bool F32S>
 static void col_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* qt,
                          int64_t ldq, void* st, hipStream_t stream) {
   const uint32_t ngt = (uint32_t)((rows + 127) / 128);
-  const dim3 grid((uint32_t)((cols + 127) / 128), ngt);
+  const dim3 grid((uint32_t)((cols + 127) / 128) * ngt);
   hipLaunchKernelGGL((quant_col_t_kernel<InT, FMT, F32S>), grid, dim3(kThreads), 0, stream, (const InT*)x,
                      (uint32_t)rows, (uint32_t)cols, ldx, qt, ldq, st, ngt);
 }
@@ -568,7 +582,7 @@ template <typename InT, int FMT>
 static void dual_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
                           uint8_t* s, uint8_t* qt, int64_t ldqt, uint8_t* st, hipStream_t stream) {
   const uint32_t ngc = (uint32_t)((cols + 127) / 128), ngt = (uint32_t)((rows + 127) / 128);
-  hipLaunchKernelGGL((quant_dual_kernel<InT, FMT>), dim3(ngc, ngt), dim3(kThreads), 0, stream, (const InT*)x,
+  hipLaunchKernelGGL((quant_dual_kernel<InT, FMT>), dim3(ngc * ngt), dim3(kThreads), 0, stream, (const InT*)x,
                      (uint32_t)rows, (uint32_t)cols, ldx, q, ldq, s, qt, ldqt, st, ngc, ngt);
 }
 
@@ -588,7 +602,7 @@ static void block_dual_dispatch(const void* w, int64_t rows, int64_t cols, int64
                                 int64_t ldq, uint8_t* s, uint8_t* qt, int64_t ldqt, uint8_t* st,
                                 hipStream_t stream) {
   const uint32_t nbc = (uint32_t)((cols + 127) / 128), nbr = (uint32_t)((rows + 127) / 128);
-  hipLaunchKernelGGL((quant_block_dual_kernel<InT, FMT>), dim3(nbc, nbr), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((quant_block_dual_kernel<InT, FMT>), dim3(nbc * nbr), dim3(kThreads), 0, stream,
                      (const InT*)w, (uint32_t)rows, (uint32_t)cols, ldw, q, ldq, s, qt, ldqt, st, nbc, nbr);
 }
 
@@ -608,7 +622,7 @@ template <typename InT, int FMT, bool F32S>
 static void block_dispatch(const void* w, int64_t rows, int64_t cols, int64_t ldw, uint8_t* q,
                            int64_t ldq, void* s, hipStream_t stream) {
   const uint32_t nbc = (uint32_t)((cols + 127) / 128);
-  const dim3 grid(nbc, (uint32_t)((rows + 127) / 128));
+  const dim3 grid(nbc * (uint32_t)((rows + 127) / 128));
   hipLaunchKernelGGL((quant_block_kernel<InT, FMT, F32S>), grid, dim3(kThreads), 0, stream, (const InT*)w,
                      (uint32_t)rows, (uint32_t)cols, ldw, q, ldq, s, nbc);
 }

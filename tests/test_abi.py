@@ -98,6 +98,7 @@ def test_f32s_validation():
     assert g(K=200) == SHAPE and g(M=-1) == SHAPE and g(M=0) == OK and g(N=0, c=None) == OK
     assert g(c=None) == NULL and g(sa=None) == NULL and g(sb=None) == NULL
     assert g(lda=256) == LD and g(ldb=500) == LD and g(ldc=200) == LD and g(blay=1, ldb=128) == LD
+    assert g(lda=(1 << 24) + 16) == LD
     assert g(a=MIS) == ALIGN and g(c=MIS) == ALIGN and g(sa=S + 2) == ALIGN and g(sb=P2 + 3) == ALIGN
     assert g(c=X) == ALIAS and g(c=S) == ALIAS and g(c=P2) == ALIAS
 
@@ -162,6 +163,7 @@ def test_gemm_validation():
     assert gemm(c=None) == NULL and gemm(a=None) == NULL and gemm(sb=None) == NULL
     assert gemm(lda=256) == LD and gemm(ldb=500) == LD and gemm(ldc=200) == LD
     assert gemm(blay=1, ldb=128) == LD  # KN: ldb >= N
+    assert gemm(lda=(1 << 24) + 16) == LD and gemm(ldb=(1 << 24) + 16) == LD  # 32-bit tile offsets
     assert gemm(a=MIS) == ALIGN and gemm(c=MIS) == ALIGN
     assert gemm(c=X) == ALIAS and gemm(c=S) == ALIAS
 
@@ -176,6 +178,7 @@ def test_mx_gemm_validation():
     assert mxg(M=0, a=None, sa=None) == OK and mxg(N=0, c=None) == OK
     assert mxg(c=None) == NULL and mxg(b=None) == NULL and mxg(sa=None) == NULL and mxg(sb=None) == NULL
     assert mxg(lda=496) == LD and mxg(ldb=520) == LD and mxg(ldc=255) == LD
+    assert mxg(lda=(1 << 24) + 16) == LD and mxg(ldb=(1 << 24) + 16) == LD
     assert mxg(a=MIS) == ALIGN and mxg(c=MIS) == ALIGN
     assert mxg(sa=S + 2) == ALIGN and mxg(sb=P2 + 1) == ALIGN
     assert mxg(c=X) == ALIAS and mxg(c=Q) == ALIAS and mxg(c=S) == ALIAS and mxg(c=P2) == ALIAS

@@ -82,3 +82,13 @@ def test_dgrad_weight_full_size():
     out = mx.gaussws(dev(w), torch.from_numpy(bt).cuda(), 2025, 7)
     torch.cuda.synchronize()
     assert np.array_equal(bits(out), oracle.gaussws(w, bt, 2025, 7, threads=ORACLE_THREADS))
+
+
+def test_tall_input_beyond_65535_strip_rows():
+    """More than 65535 strips of 32 rows: the sampler runs on a 1-D grid."""
+    rows, cols = 65536 * 32 + 32, 8
+    w = synth.weights_like(124, (rows, cols), bf16=False)
+    bt = bitwidths(125, rows, cols)
+    out = mx.gaussws(dev_ld16(w), torch.from_numpy(bt).cuda(), 3, 4)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), oracle.gaussws(w, bt, 3, 4, threads=ORACLE_THREADS))

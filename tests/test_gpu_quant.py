@@ -167,3 +167,20 @@ def test_outputs_fully_written_and_deterministic():
         assert st == 0
         torch.cuda.synchronize()
         assert torch.equal(q, q0) and torch.equal(s, s0)
+
+
+def test_tall_inputs_beyond_65535_tile_rows():
+    """More than 65535 tiles along the rows (a 2-D grid's y limit): the tile
+    kernels run on 1-D grids.  Block and transposed-column codes of an
+    8,388,736 x 16 bf16 tensor against the oracle."""
+    rows, cols = 65536 * 128 + 128, 16
+    x = synth.weights_like(123, (rows, cols), bf16=True)
+    xd = dev(x)
+    q, s = mx.quantize_block(xd, mx.E4M3)
+    qt, st = mx.quantize_token(xd, mx.E4M3, mx.COL_T)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_block(x, oracle.E4M3, threads=16)
+    assert np.array_equal(host(s), s_ref) and np.array_equal(host(q), q_ref)
+    del q, q_ref
+    qt_ref, st_ref = oracle.quantize_cols_t(x, oracle.E4M3, threads=16)
+    assert np.array_equal(host(st), st_ref) and np.array_equal(host(qt), qt_ref)
