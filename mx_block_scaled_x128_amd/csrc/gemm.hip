@@ -137,6 +137,16 @@ __device__ __forceinline__ void mfma_retire_pad() {
 #define MXFP8_GEMM_DS_SPAN 3
 #endif
 
+// LDS of one tile body (bytes): two K-block buffers of PB bytes each, and the
+// scale-group areas (SGRP bytes).  See gemm_tile for the layouts.
+template <int BM, int BN>
+struct TileLds {
+  static constexpr int A_ST = BM * 128, B_ST = BN * 128;
+  static constexpr int STG = 4 * 32 * (BN / 2 * 4 + 16);  // epilogue staging (fp32 strips)
+  static constexpr int PB = A_ST + B_ST > STG ? A_ST + B_ST : STG;
+  static constexpr int SGRP = 2 * 2 * kThreads * 4 * 4;
+};
+
 // MXS: MX operands -- scales per (row, 32-wide K block) for A ([M][K/32])
 // and for B stored [N][K] ([N][K/32]); otherwise one scale per 128-wide K
 // block (A [M][K/128]; B per row or per 128x128 tile of its storage).
@@ -145,12 +155,18 @@ __device__ __forceinline__ void mfma_retire_pad() {
 // matrix cores with unit scales into a temporary tile, which is then added
 // into the accumulators times the block's scale product (one FMA per
 // element, with a per-column multiply when B's scales are per column).
+//
+// gemm_tile is the body of one workgroup's tile (work item wg of nwg in its
+// launch); the kernels below host it on their own LDS arrays (kbuf0, kbuf1:
+// TileLds::PB bytes each, sgrp: TileLds::SGRP bytes, all 1024-byte aligned),
+// one array per buffer so that every access names its buffer.
 template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool F32S>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
+__device__ __forceinline__ void gemm_tile(
     int M, int N, int K, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ SA,
     const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ SB, void* __restrict__ C,
-    int64_t ldc, int out_bf16, int tiles_m, int tiles_n, int tile_first, int split) {
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+    int64_t ldc, int out_bf16, int tiles_m, int tiles_n, int tile_first, int split, int wg_in, int nwg_in,
+    uint8_t* kbuf0, uint8_t* kbuf1, uint8_t* sgrp) {
+#if defined(__HIP_DEVICE_COMPILE__)  // device code only
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int MT = WM / 32, NT = WN / 32;          // 32x32 MFMA tiles per wave
   static_assert(!MXS || (!BKN && BROW), "MX scales: B stored [N][K], scales per row");
@@ -165,9 +181,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // halves in different stages fetched every line twice.  (A buffer also
   // hosts the epilogue's staging, hence its size.)
   constexpr int KBB = 128;                           // K bytes per buffer row
-  constexpr int A_ST = BM * KBB, B_ST = BN * KBB;
-  constexpr int STG = 4 * 32 * (BN / 2 * 4 + 16);    // epilogue staging (fp32 strips)
-  constexpr int PB = A_ST + B_ST > STG ? A_ST + B_ST : STG;
+  constexpr int A_ST = TileLds<BM, BN>::A_ST, B_ST = TileLds<BM, BN>::B_ST;
+  constexpr int PB = TileLds<BM, BN>::PB;
   constexpr int A_LOADS = A_ST / (kThreads * 16), B_LOADS = B_ST / (kThreads * 16);  // per K block, per thread
   constexpr int CPR = BN / 16;
   static_assert(BM % 64 == 0 && BN % 64 == 0 && A_LOADS >= 1 && B_LOADS >= 1, "tile");
@@ -182,15 +197,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // once per K block (rows are nkb bytes apart in [rows][K/128] scales).
   constexpr int SG_OP = kThreads * 4 * 4;            // one operand's group area (bytes)
   constexpr int SG = 2 * SG_OP;                      // A then B
+  static_assert(2 * SG == TileLds<BM, BN>::SGRP, "scale group areas");
   (void)STAGES;
 
-  // One array per buffer; every access names its buffer with a compile-time
-  // constant (the loops below are unrolled so that it does), so the compiler
-  // can tell the buffers apart and does not drain in-flight LDS-bound loads
-  // into one buffer before reading the other.
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[PB];
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[PB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sgrp[2 * SG];
+  // Every access names its buffer with a compile-time constant (the loops
+  // below are unrolled so that it does), so the compiler can tell the buffers
+  // apart and does not drain in-flight LDS-bound loads into one buffer before
+  // reading the other.
   auto buf_ptr = [&](int p) __attribute__((always_inline)) -> uint8_t* { return p == 0 ? kbuf0 : kbuf1; };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -204,8 +217,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   // BM x BN quadrants (one workgroup each).  Workgroup ids are first
   // remapped so that each XCD (ids are dealt round-robin to the 8 XCDs)
   // walks a contiguous band of that order.
-  int wg = blockIdx.x;
-  const int nwg = gridDim.x;
+  int wg = wg_in;
+  const int nwg = nwg_in;
   if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
   const int cell = tile_first + (wg >> (2 * split));
   const int quad = wg & ((1 << (2 * split)) - 1);
@@ -732,6 +745,51 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
 #endif
 }
 
+template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool F32S>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
+    int M, int N, int K, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ SA,
+    const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ SB, void* __restrict__ C,
+    int64_t ldc, int out_bf16, int tiles_m, int tiles_n, int tile_first, int split) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef TileLds<BM, BN> L;
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[L::PB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[L::PB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sgrp[L::SGRP];
+  gemm_tile<BM, BN, STAGES, AFMT, BFMT, BKN, BROW, MXS, F32S>(M, N, K, A, lda, SA, B, ldb, SB, C, ldc, out_bf16,
+                                                             tiles_m, tiles_n, tile_first, split, blockIdx.x,
+                                                             gridDim.x, kbuf0, kbuf1, sgrp);
+#endif
+}
+
+// 256x256 tiles for cells 0 .. big - 1 (workgroups 0 .. big - 1), then the
+// remaining cells as 128x128 quadrants (the workgroups after them), in one
+// launch.  Workgroups start in id order as compute units free up, so the
+// quadrants begin on each compute unit as soon as its last 256x256 tile
+// retires, while that tile's output stores still drain; launched separately
+// they would wait for the whole first kernel to finish.  big is a multiple of
+// 8, so both parts keep their per-XCD bands.
+template <int AFMT, int BFMT, bool BKN, bool BROW, bool MXS>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bs_split_tail_kernel(
+    int M, int N, int K, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ SA,
+    const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ SB, void* __restrict__ C,
+    int64_t ldc, int out_bf16, int tiles_m, int tiles_n, int big) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef TileLds<256, 256> L;
+  static_assert(TileLds<128, 128>::PB <= L::PB && TileLds<128, 128>::SGRP <= L::SGRP, "quadrant LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[L::PB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[L::PB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sgrp[L::SGRP];
+  const int b = blockIdx.x;
+  if (b < big)
+    gemm_tile<256, 256, 4, AFMT, BFMT, BKN, BROW, MXS, false>(M, N, K, A, lda, SA, B, ldb, SB, C, ldc, out_bf16,
+                                                              tiles_m, tiles_n, 0, 0, b, big, kbuf0, kbuf1, sgrp);
+  else
+    gemm_tile<128, 128, 4, AFMT, BFMT, BKN, BROW, MXS, false>(M, N, K, A, lda, SA, B, ldb, SB, C, ldc, out_bf16,
+                                                              tiles_m, tiles_n, big, 1, b - big,
+                                                              (int)gridDim.x - big, kbuf0, kbuf1, sgrp);
+#endif
+}
+
 template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool F32S = false>
 void launch_tile(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
                  const uint8_t* b, int64_t ldb, const uint8_t* sb, void* c, int64_t ldc, int c_dtype,
@@ -782,12 +840,17 @@ void launch_shape(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda
   // in one round of 128x128 tiles, that round takes about a quarter as long.
   const int tail = big_tiles % cus;
   const bool split_tail = MXFP8_GEMM_TILE == 0 && big_tiles > cus && tail > 0 && 4 * tail <= cus;
-  const int main_cells = split_tail ? big_tiles - tail : big_tiles;
-  launch_tile<256, 256, 4, AFMT, BFMT, BKN, BROW, MXS>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, bm, bn, 0,
-                                                  main_cells, 0, stream);
-  if (split_tail)
-    launch_tile<128, 128, 4, AFMT, BFMT, BKN, BROW, MXS>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, bm, bn,
-                                                    main_cells, tail, 1, stream);
+  if (!split_tail) {
+    launch_tile<256, 256, 4, AFMT, BFMT, BKN, BROW, MXS>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, bm, bn,
+                                                    0, big_tiles, 0, stream);
+    return;
+  }
+  // main_cells is a multiple of the CU count (256 = 8 XCDs x 32), so both
+  // parts of the launch keep their per-XCD bands.
+  const int main_cells = big_tiles - tail;
+  hipLaunchKernelGGL((gemm_bs_split_tail_kernel<AFMT, BFMT, BKN, BROW, MXS>), dim3(main_cells + 4 * tail),
+                     dim3(kThreads), 0, stream, (int)M, (int)N, (int)K, a, lda, sa, b, ldb, sb, c, ldc,
+                     c_dtype == 1 ? 1 : 0, bm, bn, main_cells);
 }
 
 template <int AFMT, int BFMT>

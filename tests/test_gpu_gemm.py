@@ -139,7 +139,8 @@ def test_end_to_end_quantize_then_gemm_small():
 @pytest.mark.parametrize("bf16_out", [False, True])
 def test_short_last_round_as_quadrants(b_layout, b_scale, bf16_out):
     """17 x 16 cells of 256x256 on 256 CUs: the last 16 cells run as 128x128
-    quadrants in a second launch, some of them wholly past the M edge.  The
+    quadrants after the 256x256 tiles, in the same launch, some of them wholly
+    past the M edge.  The
     quadrant rows are compared with the oracle in full, the rest on samples
     (a band across the last full cell row and random points)."""
     M, N, K = 256 * 16 + 100, 256 * 16 - 30, 256
