@@ -141,7 +141,8 @@ def add_context(line, step, timer):
         if name in line["kernels"]:
             line["kernels"][name].update(d)
     line["device"] = device
-    line["timing"] = ("value: graph replays of the whole step between synchronisations; kernels.us: mean of "
+    line["timing"] = ("value: replays of a graph of steps_per_graph whole steps between synchronisations; "
+                      "kernels.us: mean of "
                       "event-bracketed eager calls (us_median: median); us_cold_median: each call after a "
                       "512 MiB scrub write, medians of 10")
     return line
@@ -152,17 +153,29 @@ class _NoTimer:
         return fn()
 
 
+def steps_per_graph(steps, cap=10):
+    """Steps captured in one graph: the largest divisor of `steps` up to `cap`, so that
+    whole replays cover exactly `steps` steps."""
+    return max(d for d in range(1, min(cap, steps) + 1) if steps % d == 0)
+
+
 def time_graph(step, steps, warmup, outputs):
-    """Captures one step in a HIP graph, checks that a replay reproduces the eager step's
-    outputs bit for bit, then times `steps` replays (after `warmup`) between device
-    synchronisations.  Returns seconds per step."""
+    """Captures S consecutive steps in one HIP graph (S = steps_per_graph(steps): a
+    replay of a graph launch costs the device an idle gap of ~8 us before its first
+    kernel, which one step per graph would pay every step), checks that a replay
+    reproduces the eager step's outputs bit for bit, then times steps / S replays
+    (after warmup / S, rounded up) between device synchronisations.  Every step is the
+    whole path on the same batch.  Returns (seconds per step, S)."""
     import torch
+    steps = max(1, steps)
+    per_graph = steps_per_graph(steps)
     step(_NoTimer())
     torch.cuda.synchronize()
     ref = [o.clone() for o in outputs]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        step(_NoTimer())
+        for _ in range(per_graph):
+            step(_NoTimer())
     for o in outputs:
         o.zero_()
     g.replay()
@@ -170,14 +183,14 @@ def time_graph(step, steps, warmup, outputs):
     for o, r in zip(outputs, ref):
         if not torch.equal(o, r):
             raise RuntimeError("graph replay differs from the eager step")
-    for _ in range(warmup):
+    for _ in range(-(-warmup // per_graph)):
         g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for _ in range(steps // per_graph):
         g.replay()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    return (time.perf_counter() - t0) / steps, per_graph
 
 
 def time_steps(step, steps, warmup):
@@ -300,7 +313,7 @@ def bench_fprop(args):
     N = t["w"].shape[0]
     step, outputs = fprop_step_fn(t)
     per_step_eager, timer = time_steps(step, args.steps, args.warmup)
-    per_step = time_graph(step, args.steps, args.warmup, outputs)
+    per_step, per_graph = time_graph(step, args.steps, args.warmup, outputs)
     flops = 2.0 * M * N * K
     g = timer.mean("gemm")
     qx = timer.mean("quant_token_x")
@@ -311,7 +324,7 @@ def bench_fprop(args):
     line = {
         "metric": METRIC, "value": round(flops / per_step / 1e12, 3), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(per_step * 1e3, 4),
-        "ms_per_step_eager": round(per_step_eager * 1e3, 4),
+        "ms_per_step_eager": round(per_step_eager * 1e3, 4), "steps_per_graph": per_graph,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
         "data": "synthetic (seeded numpy PCG64; bf16 inputs resident in HBM before timing)",
         "config": {"workload": "fprop1p5b: token-quantize X 4096x1536 bf16 (1x128, E4M3) + block-quantize "
@@ -528,7 +541,7 @@ def bench_other(args):
         M = N = K = 0
         desc = "mxstress: 64 tensors 4096x4096 fp32, MX 32-element E4M3 blocks, OCP floor scales, clamp counts"
     per_step_eager, timer = time_steps(step, args.steps, args.warmup)
-    per_step = time_graph(step, args.steps, args.warmup, outputs)
+    per_step, per_graph = time_graph(step, args.steps, args.warmup, outputs)
     for name, b in sizes.items():
         t = timer.mean(name)
         kern[name] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
@@ -549,7 +562,8 @@ def bench_other(args):
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(per_step * 1e3, 4),
-        "ms_per_step_eager": round(per_step_eager * 1e3, 4), "higher_is_better": True,
+        "ms_per_step_eager": round(per_step_eager * 1e3, 4), "steps_per_graph": per_graph,
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8", "data": "synthetic (seeded numpy PCG64)",
         "config": {"workload": desc, "M": M, "N": N, "K": K}, "kernels": kern, "roofline": roof,
         "cpu_baseline": None,
