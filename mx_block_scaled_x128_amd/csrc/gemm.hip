@@ -164,7 +164,7 @@ template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, b
 __device__ __forceinline__ void gemm_tile(
     int M, int N, int K, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ SA,
     const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ SB, void* __restrict__ C,
-    int64_t ldc, int out_bf16, int tiles_m, int tiles_n, int tile_first, int split, int wg_in, int nwg_in,
+    int64_t ldc, int out_bf16, int tiles_m, int tiles_n, int tile_first, int sm, int sn, int wg_in, int nwg_in,
     uint8_t* kbuf0, uint8_t* kbuf1, uint8_t* sgrp) {
 #if defined(__HIP_DEVICE_COMPILE__)  // device code only
   constexpr int WM = BM / 2, WN = BN / 2;
@@ -211,25 +211,25 @@ __device__ __forceinline__ void gemm_tile(
   const int wm = wave >> 1, wn = wave & 1;
 
   // ---- tile of this workgroup.  Tiles are enumerated over a grid of
-  // tiles_m x tiles_n cells of (BM << split) x (BN << split), in groups of
-  // GROUP cell rows walked column by column; this launch covers cells
-  // tile_first, tile_first + 1, ... and, with split = 1, each cell as four
-  // BM x BN quadrants (one workgroup each).  Workgroup ids are first
+  // tiles_m x tiles_n cells of (BM << sm) x (BN << sn), in groups of GROUP
+  // cell rows walked column by column; this launch covers cells tile_first,
+  // tile_first + 1, ... and each cell as 2^sm x 2^sn BM x BN sub-tiles (one
+  // workgroup each; sm = sn = 0: the cell itself).  Workgroup ids are first
   // remapped so that each XCD (ids are dealt round-robin to the 8 XCDs)
   // walks a contiguous band of that order.
   int wg = wg_in;
   const int nwg = nwg_in;
   if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
-  const int cell = tile_first + (wg >> (2 * split));
-  const int quad = wg & ((1 << (2 * split)) - 1);
+  const int cell = tile_first + (wg >> (sm + sn));
+  const int sub = wg & ((1 << (sm + sn)) - 1);
   constexpr int GROUP = 8;
   const int group = cell / (GROUP * tiles_n);
   const int first = group * GROUP;
   const int gsz = min(tiles_m - first, GROUP);
   const int within = cell - group * GROUP * tiles_n;
-  const int m0 = (((first + within % gsz) << split) + (quad >> split)) * BM;
-  const int n0 = (((within / gsz) << split) + (quad & split)) * BN;
-  if (m0 >= M || n0 >= N) return;  // a quadrant past the matrix edge (uniform per workgroup)
+  const int m0 = (((first + within % gsz) << sm) + (sub >> sn)) * BM;
+  const int n0 = (((within / gsz) << sn) + (sub & ((1 << sn) - 1))) * BN;
+  if (m0 >= M || n0 >= N) return;  // a sub-tile past the matrix edge (uniform per workgroup)
 
   const int nkb = K >> 7;   // 128-wide K blocks (= scale blocks)
   const int nnb = (N + 127) >> 7;
@@ -749,25 +749,28 @@ template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, b
 __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ SA,
     const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ SB, void* __restrict__ C,
-    int64_t ldc, int out_bf16, int tiles_m, int tiles_n, int tile_first, int split) {
+    int64_t ldc, int out_bf16, int tiles_m, int tiles_n, int tile_first) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef TileLds<BM, BN> L;
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[L::PB];
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[L::PB];
   __shared__ __attribute__((aligned(1024))) uint8_t sgrp[L::SGRP];
   gemm_tile<BM, BN, STAGES, AFMT, BFMT, BKN, BROW, MXS, F32S>(M, N, K, A, lda, SA, B, ldb, SB, C, ldc, out_bf16,
-                                                             tiles_m, tiles_n, tile_first, split, blockIdx.x,
+                                                             tiles_m, tiles_n, tile_first, 0, 0, blockIdx.x,
                                                              gridDim.x, kbuf0, kbuf1, sgrp);
 #endif
 }
 
 // 256x256 tiles for cells 0 .. big - 1 (workgroups 0 .. big - 1), then the
-// remaining cells as 128x128 quadrants (the workgroups after them), in one
-// launch.  Workgroups start in id order as compute units free up, so the
-// quadrants begin on each compute unit as soon as its last 256x256 tile
-// retires, while that tile's output stores still drain; launched separately
-// they would wait for the whole first kernel to finish.  big is a multiple of
-// 8, so both parts keep their per-XCD bands.
+// remaining cells as 128x128 quadrants (the kTailSub workgroups per cell
+// after them), in one launch.  Workgroups start in id order as compute units
+// free up, so the quadrants begin on each compute unit as soon as its last
+// 256x256 tile retires, while that tile's output stores still drain;
+// launched separately they would wait for the whole first kernel to finish.
+// big is a multiple of 8, so both parts keep their per-XCD bands.  (256x128
+// halves instead of quadrants, half as many workgroups, took 3 us longer on
+// the 4096x8960x1536 shape.)
+constexpr int kTailSub = 4;
 template <int AFMT, int BFMT, bool BKN, bool BROW, bool MXS>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bs_split_tail_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ SA,
@@ -782,10 +785,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_split_tail_kernel(
   const int b = blockIdx.x;
   if (b < big)
     gemm_tile<256, 256, 4, AFMT, BFMT, BKN, BROW, MXS, false>(M, N, K, A, lda, SA, B, ldb, SB, C, ldc, out_bf16,
-                                                              tiles_m, tiles_n, 0, 0, b, big, kbuf0, kbuf1, sgrp);
+                                                              tiles_m, tiles_n, 0, 0, 0, b, big, kbuf0, kbuf1,
+                                                              sgrp);
   else
     gemm_tile<128, 128, 4, AFMT, BFMT, BKN, BROW, MXS, false>(M, N, K, A, lda, SA, B, ldb, SB, C, ldc, out_bf16,
-                                                              tiles_m, tiles_n, big, 1, b - big,
+                                                              tiles_m, tiles_n, big, 1, 1, b - big,
                                                               (int)gridDim.x - big, kbuf0, kbuf1, sgrp);
 #endif
 }
@@ -793,11 +797,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_split_tail_kernel(
 template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool F32S = false>
 void launch_tile(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
                  const uint8_t* b, int64_t ldb, const uint8_t* sb, void* c, int64_t ldc, int c_dtype,
-                 int tiles_m, int tiles_n, int tile_first, int cells, int split, hipStream_t stream) {
+                 int tiles_m, int tiles_n, int tile_first, int cells, hipStream_t stream) {
   if (cells <= 0) return;
-  hipLaunchKernelGGL((gemm_bs_kernel<BM, BN, STAGES, AFMT, BFMT, BKN, BROW, MXS, F32S>), dim3(cells << (2 * split)),
+  hipLaunchKernelGGL((gemm_bs_kernel<BM, BN, STAGES, AFMT, BFMT, BKN, BROW, MXS, F32S>), dim3(cells),
                      dim3(kThreads), 0, stream, (int)M, (int)N, (int)K, a, lda, sa, b, ldb, sb, c, ldc,
-                     c_dtype == 1 ? 1 : 0, tiles_m, tiles_n, tile_first, split);
+                     c_dtype == 1 ? 1 : 0, tiles_m, tiles_n, tile_first);
 }
 
 // Compute units of the current device (cached per device; concurrent first
@@ -833,22 +837,22 @@ void launch_shape(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda
   if (!big) {
     const int sm = (int)((M + 127) / 128), sn = (int)((N + 127) / 128);
     launch_tile<128, 128, 4, AFMT, BFMT, BKN, BROW, MXS>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, sm, sn, 0,
-                                                    sm * sn, 0, stream);
+                                                    sm * sn, stream);
     return;
   }
-  // Last partial round: when its 256x256 tiles, cut in four, fit on the CUs
-  // in one round of 128x128 tiles, that round takes about a quarter as long.
+  // Last partial round: when its 256x256 tiles, cut in kTailSub, fit on the
+  // CUs in one round of sub-tiles, that round takes a fraction as long.
   const int tail = big_tiles % cus;
-  const bool split_tail = MXFP8_GEMM_TILE == 0 && big_tiles > cus && tail > 0 && 4 * tail <= cus;
+  const bool split_tail = MXFP8_GEMM_TILE == 0 && big_tiles > cus && tail > 0 && kTailSub * tail <= cus;
   if (!split_tail) {
     launch_tile<256, 256, 4, AFMT, BFMT, BKN, BROW, MXS>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, bm, bn,
-                                                    0, big_tiles, 0, stream);
+                                                    0, big_tiles, stream);
     return;
   }
   // main_cells is a multiple of the CU count (256 = 8 XCDs x 32), so both
   // parts of the launch keep their per-XCD bands.
   const int main_cells = big_tiles - tail;
-  hipLaunchKernelGGL((gemm_bs_split_tail_kernel<AFMT, BFMT, BKN, BROW, MXS>), dim3(main_cells + 4 * tail),
+  hipLaunchKernelGGL((gemm_bs_split_tail_kernel<AFMT, BFMT, BKN, BROW, MXS>), dim3(main_cells + kTailSub * tail),
                      dim3(kThreads), 0, stream, (int)M, (int)N, (int)K, a, lda, sa, b, ldb, sb, c, ldc,
                      c_dtype == 1 ? 1 : 0, bm, bn, main_cells);
 }
@@ -874,13 +878,13 @@ void launch_f32s_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t 
   const int sm = (int)((M + 127) / 128), sn = (int)((N + 127) / 128);
   if (b_layout == 1)
     launch_tile<128, 128, 4, AFMT, BFMT, true, false, false, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype,
-                                                                  sm, sn, 0, sm * sn, 0, stream);
+                                                                  sm, sn, 0, sm * sn, stream);
   else if (b_scale_mode == 1)
     launch_tile<128, 128, 4, AFMT, BFMT, false, true, false, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype,
-                                                                  sm, sn, 0, sm * sn, 0, stream);
+                                                                  sm, sn, 0, sm * sn, stream);
   else
     launch_tile<128, 128, 4, AFMT, BFMT, false, false, false, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc,
-                                                                   c_dtype, sm, sn, 0, sm * sn, 0, stream);
+                                                                   c_dtype, sm, sn, 0, sm * sn, stream);
 }
 
 }  // namespace gemm_detail
