@@ -133,8 +133,8 @@ def test_quantize_then_gemm_strict_bound(x_dtype, a_fmt, b_fmt):
 @pytest.mark.parametrize("bf16_out", [False, True])
 def test_short_last_round_as_quadrants(bf16_out):
     """17 x 16 cells of 256x256 on 256 CUs: the last 16 cells run as 128x128
-    quadrants in a second launch.  Quadrant rows compared in full, the rest on
-    samples."""
+    quadrants after the 256x256 tiles, in the same launch.  Quadrant rows
+    compared in full, the rest on samples."""
     M, N, K = 256 * 16 + 100, 256 * 16 - 30, 256
     seed = 177 + bf16_out
     a = synth.random_codes(seed, (M, K), 0)
