@@ -20,7 +20,8 @@ MX operands: 32-element E8M0 scales for X and W, mx_gemm), f32sfprop1p5b
 two-orientation quantizers on the wgrad activation and the dgrad weight),
 gaussws7b (GaussWS sampling of the dgrad weight from fp32 master weights),
 mxstress -- for the per-kernel roofline figures; they print the same kind of
-JSON line.
+JSON line.  gemmsweep times the GEMM alone over N and K (M = 4096) and fits
+the per-round fixed cost; copy times a plain 256 MiB device copy.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 """
@@ -44,7 +45,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="fprop1p5b",
                    choices=["fprop1p5b", "dgrad7b", "wgrad", "mxfprop1p5b", "f32sfprop1p5b", "dualq", "gaussws7b",
-                            "mxstress", "copy"])
+                            "mxstress", "copy", "gemmsweep"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-rows", type=int, default=0,
                    help="token rows in the oracle sample (0 = all rows: the full step)")
@@ -351,6 +352,60 @@ def bench_fprop(args):
     return line
 
 
+def bench_gemm_sweep(args):
+    """The block-scaled GEMM at M = 4096 over N and K, bf16 output (and fp32 output at one
+    shape), uniformly random finite E4M3 codes with scale bytes in [120, 134]: one round of
+    256x256 tiles at N = 4096 (256 tiles, one per CU), two rounds at N = 8192.  Per shape,
+    `warmup` calls and then `steps` calls back to back between one event pair (mean per
+    call).  A least-squares line through the one-round bf16 points, time = fixed + slope x
+    (K / 128), separates the cost of a round that does not scale with K (prologue, output
+    write) from the K loop."""
+    import torch
+    import mx_block_scaled_x128_amd as mx
+    import synth
+    M = 4096
+    shapes = [(4096, 256, True), (4096, 512, True), (4096, 1536, True), (4096, 3072, True), (4096, 6144, True),
+              (8192, 1536, True), (4096, 1536, False)]
+    res = []
+    for i, (N, K, bf16) in enumerate(shapes):
+        a = torch.from_numpy(synth.random_codes(7000 + 4 * i, (M, K), 0)).cuda()
+        b = torch.from_numpy(synth.random_codes(7001 + 4 * i, (N, K), 0)).cuda()
+        sa = torch.from_numpy(synth.random_scale_bytes(7002 + 4 * i, (M, K // 128))).cuda()
+        sb = torch.from_numpy(synth.random_scale_bytes(7003 + 4 * i, (N // 128, K // 128))).cuda()
+        out = torch.empty((M, N), dtype=torch.bfloat16 if bf16 else torch.float32, device="cuda")
+
+        def call():
+            mx.block_scaled_gemm(a, sa, mx.E4M3, b, sb, mx.E4M3, mx.B_NK, mx.SCALE_BLOCK128, out=out)
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        res.append({"M": M, "N": N, "K": K, "out": "bf16" if bf16 else "fp32", "us": round(us, 2),
+                    "TFLOP/s": round(2.0 * M * N * K / us / 1e6, 1)})
+        del a, b, sa, sb, out
+    one = [r for r in res if r["N"] == 4096 and r["out"] == "bf16"]
+    x = np.array([r["K"] / 128.0 for r in one])
+    y = np.array([r["us"] for r in one])
+    slope, fixed = np.polyfit(x, y, 1)
+    best = max(res, key=lambda r: r["TFLOP/s"])
+    return {"metric": "block-scaled FP8 GEMM TFLOP/s over N and K (M = 4096)", "value": best["TFLOP/s"],
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(best["us"] / 1e3, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic (random finite codes)",
+            "config": {"workload": "gemmsweep: M=4096, N in {4096, 8192}, K in {256 .. 6144}"},
+            "sweep": res, "fit_one_round_bf16": {"fixed_us": round(float(fixed), 2),
+                                                 "us_per_k_block": round(float(slope), 3)},
+            "roofline": {"bound": "mfma", "achieved": best["TFLOP/s"], "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(best["TFLOP/s"] / FP8_PEAK_TFLOPS, 4), "traffic": None},
+            "cpu_baseline": None}
+
+
 def bench_copy(args):
     """A plain device copy of 256 MiB (torch's copy kernel): the reference point that scales
     profiler byte counters (FETCH_SIZE / WRITE_SIZE) to bytes, and a measured bandwidth."""
@@ -589,6 +644,8 @@ def main():
         line = bench_fprop(args)
     elif args.workload == "copy":
         line = bench_copy(args)
+    elif args.workload == "gemmsweep":
+        line = bench_gemm_sweep(args)
     else:
         line = bench_other(args)
     print(json.dumps(line), flush=True)
