@@ -9,8 +9,8 @@
 //
 // Every kernel reads its input once (16-byte vector loads, 8 elements per
 // lane), reduces amax with DPP inside the wavefront (LDS only where a group
-// spans waves), and writes packed codes (8 bytes per lane) with non-temporal
-// stores.
+// spans waves), and writes packed codes (8 bytes per lane) with ordinary
+// stores, which leave them in the last-level cache for the GEMM.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -82,7 +82,7 @@ __device__ __forceinline__ void store_row_tile(const uint8_t* rtile, uint8_t* __
     const uint32_t r = idx >> 3, p = idx & 7;
     if (r0 + r < rows && c0 + p * 16 < cols) {
       const uint4 v = *reinterpret_cast<const uint4*>(rtile + r * 128 + ((p ^ ((r >> 3) & 7)) << 4));
-      store_nt(q + (int64_t)(r0 + r) * ldq + c0 + p * 16, v);
+      store_codes(q + (int64_t)(r0 + r) * ldq + c0 + p * 16, v);
     }
   }
 }
@@ -98,7 +98,7 @@ __device__ __forceinline__ void store_tile_t(const uint8_t* tile, uint8_t* __res
     if (c0 + ch < cols && t0 + ck * 16 < rows) {
       const uint2 a = *reinterpret_cast<const uint2*>(tile + ch * kColPitch + ck * 16);
       const uint2 b = *reinterpret_cast<const uint2*>(tile + ch * kColPitch + ck * 16 + 8);
-      store_nt(qt + (int64_t)(c0 + ch) * ldqt + t0 + ck * 16, make_uint4(a.x, a.y, b.x, b.y));
+      store_codes(qt + (int64_t)(c0 + ch) * ldqt + t0 + ck * 16, make_uint4(a.x, a.y, b.x, b.y));
     }
   }
 }
@@ -145,13 +145,13 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(
       if constexpr (F32S) {
         const float sf = scale_f32<FMT>(m);
         if (act[u])
-          store_nt(q + (int64_t)row[u] * ldq + grp[u] * 128 + sub * 8, codes8_div<FMT>(f[u], sf));
+          store_codes(q + (int64_t)row[u] * ldq + grp[u] * 128 + sub * 8, codes8_div<FMT>(f[u], sf));
         if (sub == 0 && gvalid[u]) static_cast<float*>(s)[(int64_t)row[u] * ngroups + grp[u]] = sf;
       } else {
         const int e = scale_exp_ceil<FMT>(m);
         const float sc = pow2_neg(e);
         if (act[u])
-          store_nt(q + (int64_t)row[u] * ldq + grp[u] * 128 + sub * 8, codes8<FMT>(f[u], sc));
+          store_codes(q + (int64_t)row[u] * ldq + grp[u] * 128 + sub * 8, codes8<FMT>(f[u], sc));
         if (sub == 0 && gvalid[u]) static_cast<uint8_t*>(s)[(int64_t)row[u] * ngroups + grp[u]] = (uint8_t)(e + 127);
       }
     }
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t r = r0 + tr * 8 + i;
-      if (cact && r < rows) store_nt(q + (int64_t)r * ldq + c0 + tc * 8, codes8_div<FMT>(f[i], sf));
+      if (cact && r < rows) store_codes(q + (int64_t)r * ldq + c0 + tc * 8, codes8_div<FMT>(f[i], sf));
     }
     if (tid == 0) static_cast<float*>(s)[(int64_t)b.y * nbc + b.x] = sf;
   } else {
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t r = r0 + tr * 8 + i;
-      if (cact && r < rows) store_nt(q + (int64_t)r * ldq + c0 + tc * 8, codes8<FMT>(f[i], sc));
+      if (cact && r < rows) store_codes(q + (int64_t)r * ldq + c0 + tc * 8, codes8<FMT>(f[i], sc));
     }
     if (tid == 0) static_cast<uint8_t*>(s)[(int64_t)b.y * nbc + b.x] = (uint8_t)(e + 127);
   }
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(
         uint2 o;
         o.x = cvt4<FMT>(v[0], v[1], v[2], v[3]);
         o.y = cvt4<FMT>(v[4], v[5], v[6], v[7]);
-        store_nt(q + (int64_t)row[u] * ldq + blk[u] * 32 + sub * 8, o);
+        store_codes(q + (int64_t)row[u] * ldq + blk[u] * 32 + sub * 8, o);
         if (sub == 0) {
           s[(int64_t)row[u] * nblk + blk[u]] = (uint8_t)(e + 127);
           if (COUNTS) cnt[(int64_t)row[u] * nblk + blk[u]] = (uint8_t)n;
