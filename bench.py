@@ -670,7 +670,7 @@ def bench_other(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)"
+        print("bench.py measures one GPU only: the library has no multi-GPU path (requested --gpus %d)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
