@@ -19,6 +19,10 @@ namespace mxfp8 {
 namespace quant_detail {
 
 constexpr int kThreads = 256;
+// quant_block_kernel: 8 waves per 128x128 tile, 4 rows x 8 columns per
+// thread (measured 2-5 % faster than 4 waves with 8 rows each).
+constexpr int kBlockThreads = 512;
+static_assert(kBlockThreads == 512, "quant_block_kernel's reduction reads 8 wave maxima");
 constexpr uint32_t kMaxBlocks = 256 * 8;  // 8 workgroups per CU, grid-stride beyond that
 
 // Tile kernels run on 1-D grids (a 2-D grid's y extent is limited to 65535):
@@ -387,42 +391,43 @@ __global__ __launch_bounds__(kThreads) void quant_block_dual_kernel(
 
 // ---------------------------------------------------------------------------
 // 128x128 tiles.  One workgroup per tile, the whole tile held in registers
-// (8 rows x 8 columns per thread), amax by DPP + cross-lane shuffles inside
-// each wavefront and 4 values through LDS across wavefronts; then one pass of
-// casts and 8-byte stores.  Input is read from HBM exactly once.
+// (4 rows x 8 columns per thread, 8 wavefronts), amax by DPP + cross-lane
+// shuffles inside each wavefront and 8 values through LDS across wavefronts;
+// then one pass of casts and 8-byte stores.  Input is read from HBM exactly
+// once.
 // ---------------------------------------------------------------------------
 template <typename InT, int FMT, bool F32S>
-__global__ __launch_bounds__(kThreads) void quant_block_kernel(
+__global__ __launch_bounds__(kBlockThreads) void quant_block_kernel(
     const InT* __restrict__ w, uint32_t rows, uint32_t cols, int64_t ldw, uint8_t* __restrict__ q,
     int64_t ldq, void* __restrict__ s, uint32_t nbc) {
-  __shared__ uint32_t red[4];
+  __shared__ uint32_t red[kBlockThreads / 64];
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t tc = lane & 15;               // column chunk: columns tc*8 .. tc*8+7
-  const uint32_t tr = (lane >> 4) + 4 * wv;    // row chunk: rows tr*8 .. tr*8+7
+  const uint32_t tr = (lane >> 4) + 4 * wv;    // row chunk: rows tr*4 .. tr*4+3
   const TileXY b = tile_xy(nbc);
   const uint32_t r0 = b.y * 128, c0 = b.x * 128;
   const bool cact = c0 + tc * 8 < cols;
-  float f[8][8];
+  float f[4][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t r = r0 + tr * 8 + i;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t r = r0 + tr * 4 + i;
     if (cact && r < rows) load8<false>(w + (int64_t)r * ldw + c0 + tc * 8, f[i]);
     else zero8(f[i]);
   }
   uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = max(m, abs_bits(f[i][j]));
   m = max_wave(m);
   if (lane == 0) red[wv] = m;
   __syncthreads();
-  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  m = max(max(max(red[0], red[1]), max(red[2], red[3])), max(max(red[4], red[5]), max(red[6], red[7])));
   if constexpr (F32S) {
     const float sf = scale_f32<FMT>(m);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t r = r0 + tr * 8 + i;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t r = r0 + tr * 4 + i;
       if (cact && r < rows) store_codes(q + (int64_t)r * ldq + c0 + tc * 8, codes8_div<FMT>(f[i], sf));
     }
     if (tid == 0) static_cast<float*>(s)[(int64_t)b.y * nbc + b.x] = sf;
@@ -430,8 +435,8 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(
     const int e = scale_exp_ceil<FMT>(m);
     const float sc = pow2_neg(e);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t r = r0 + tr * 8 + i;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t r = r0 + tr * 4 + i;
       if (cact && r < rows) store_codes(q + (int64_t)r * ldq + c0 + tc * 8, codes8<FMT>(f[i], sc));
     }
     if (tid == 0) static_cast<uint8_t*>(s)[(int64_t)b.y * nbc + b.x] = (uint8_t)(e + 127);
@@ -623,7 +628,7 @@ static void block_dispatch(const void* w, int64_t rows, int64_t cols, int64_t ld
                            int64_t ldq, void* s, hipStream_t stream) {
   const uint32_t nbc = (uint32_t)((cols + 127) / 128);
   const dim3 grid(nbc * (uint32_t)((rows + 127) / 128));
-  hipLaunchKernelGGL((quant_block_kernel<InT, FMT, F32S>), grid, dim3(kThreads), 0, stream, (const InT*)w,
+  hipLaunchKernelGGL((quant_block_kernel<InT, FMT, F32S>), grid, dim3(kBlockThreads), 0, stream, (const InT*)w,
                      (uint32_t)rows, (uint32_t)cols, ldw, q, ldq, s, nbc);
 }
 
