@@ -1,31 +1,34 @@
 """Benchmark of the FP8 hot path on one MI355X.
 
-One step = the forward pass of a 1.5B-class linear layer with hybrid-granularity
-FP8 (token-wise 1x128 E4M3 activations, 128x128-block E4M3 weights, UE8M0
-round-up scales) on seeded synthetic bf16 tensors already resident in HBM:
-  1. fp8_quantize_token  X [4096 x 1536] bf16 -> codes + scales
-  2. fp8_quantize_block  W [8960 x 1536] bf16 -> codes + scales
-  3. fp8_block_scaled_gemm  Y = Xq * Wq^T, M=4096 N=8960 K=1536, fp32 accumulate, bf16 out
-`value` is the whole step's throughput in TFLOP/s (2*M*N*K per step / step
-time), with the step's launches captured once in a HIP graph and replayed
-(the launches are asynchronous and allocate nothing, so a replay is the same
-work without the host's per-launch cost).  In a separate eager pass each
-entry point is timed with events on the stream it runs on, and the dominant
-one (the GEMM) is reported against the dense FP8 MFMA peak.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
+Default step (workload dgrad7b): the input-gradient pass of a 7B-class linear
+layer with hybrid-granularity FP8, on seeded synthetic bf16 tensors already
+resident in HBM:
+  1. fp8_quantize_token  dY [8192 x 18944] bf16 -> 1x128 E5M2 codes + E8M0 scales
+  2. fp8_quantize_block  W [18944 x 3584] bf16 -> 128x128 E4M3 codes + E8M0 scales
+  3. fp8_block_scaled_gemm  dX = dYq * Wq, M=8192 N=3584 K=18944 (W stored [K][N]),
+     fp32 accumulation, bf16 out
+`value` is the whole step's throughput in TFLOP/s (2*M*N*K per step / step time),
+with consecutive steps captured in a HIP graph and replayed (the launches are
+asynchronous and allocate nothing, so a replay is the same work without the host's
+per-launch cost).  In a separate eager pass each entry point is timed with events
+on the stream it runs on, and the dominant one (the GEMM) is reported against the
+dense FP8 MFMA peak (`roofline`).  `cpu_baseline` times the CPU oracle on a
+bounded sample of the same step.
 
-Other workloads (--workload): dgrad7b, wgrad, mxfprop1p5b (the fprop step on
-MX operands: 32-element E8M0 scales for X and W, mx_gemm), f32sfprop1p5b
-(the fprop step with fp32 instead of power-of-two scales), dualq (the
-two-orientation quantizers on the wgrad activation and the dgrad weight),
-gaussws7b (GaussWS sampling of the dgrad weight from fp32 master weights),
-mxstress -- for the per-kernel roofline figures; they print the same kind of
-JSON line.  gemmsweep times the GEMM alone over N and K (M = 4096) and fits
-the per-round fixed cost; copy times a plain 256 MiB device copy.
+Other workloads (--workload) print the same kind of line: fprop1p5b (forward of
+a 1.5B-class layer), wgrad (weight gradient from column-quantized activations and
+gradients), mxfprop1p5b (the forward on MX operands: 32-element E8M0 scales,
+mx_gemm), f32sfprop1p5b (the forward with fp32 instead of power-of-two scales),
+dualq (the two-orientation quantizers), gaussws7b (GaussWS sampling of the 7B
+weight from fp32 master weights), mxstress (MX quantization with clamp counts of
+64 distinct 4096x4096 fp32 tensors, with the clamp statistics).  gemmsweep times
+the GEMM alone over N and K; copy times a plain 256 MiB device copy.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+                       [--cpu-rows R]
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -36,19 +39,20 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, TFLOP/s
 METRIC = "FP8 quantize GB/s + block-scaled FP8 GEMM TFLOP/s, % of MI355X peak"
+HERE = os.path.dirname(os.path.abspath(__file__))
+WORKLOADS = ["dgrad7b", "fprop1p5b", "wgrad", "mxfprop1p5b", "f32sfprop1p5b", "dualq", "gaussws7b", "mxstress",
+             "copy", "gemmsweep"]
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="fprop1p5b",
-                   choices=["fprop1p5b", "dgrad7b", "wgrad", "mxfprop1p5b", "f32sfprop1p5b", "dualq", "gaussws7b",
-                            "mxstress", "copy", "gemmsweep"])
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="dgrad7b", choices=WORKLOADS)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--cpu-rows", type=int, default=0,
-                   help="token rows in the oracle sample (0 = all rows: the full step)")
+    p.add_argument("--cpu-rows", type=int, default=-1,
+                   help="output rows of the GEMM in the oracle sample (0 = all; default: per workload)")
     return p.parse_args()
 
 
@@ -58,6 +62,19 @@ def to_dev(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
     return torch.from_numpy(a).cuda()
 
+
+def oracle_threads():
+    """Host threads for the oracle: the machine's cores, at most 16 (the host share of
+    one GPU on the boxes this runs on)."""
+    return min(16, os.cpu_count() or 1)
+
+
+def _check(st, what):
+    if st != 0:
+        raise RuntimeError("%s returned status %d" % (what, st))
+
+
+# ------------------------------------------------------------------------ timing
 
 class KernelTimer:
     """Event pairs around each launch on the current stream; averages per kernel."""
@@ -103,6 +120,22 @@ class ColdTimer(KernelTimer):
         return super().run(name, fn)
 
 
+class _NoTimer:
+    def run(self, name, fn):
+        return fn()
+
+
+class _CaptureTimer(_NoTimer):
+    """Runs a step and keeps each named launch's closure."""
+
+    def __init__(self):
+        self.fns = {}
+
+    def run(self, name, fn):
+        self.fns[name] = fn
+        return fn()
+
+
 def context_measurements(step, timer, reps=10):
     """Median warm and cold (scrubbed) per-call times, the device description and a
     measured device copy bandwidth, added to the JSON line as context."""
@@ -134,37 +167,6 @@ def context_measurements(step, timer, reps=10):
                   "us_cold_median": round(cold.median(name) * 1e6, 2)} for name in timer.times}
     return per, {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                  "compute_units": props.multi_processor_count, "copy_256MiB_GBs": round(copy_gbs, 1)}
-
-
-def add_context(line, step, timer):
-    per, device = context_measurements(step, timer)
-    for name, d in per.items():
-        if name in line["kernels"]:
-            line["kernels"][name].update(d)
-    line["device"] = device
-    line["timing"] = ("value: replays of a graph of steps_per_graph whole steps between synchronisations; "
-                      "kernels.us: mean of "
-                      "event-bracketed eager calls inside the step (us_median: median); us_cold_median: each "
-                      "call after a 512 MiB scrub write, medians of 10; roofline.achieved: from gemm.us; "
-                      "gemm.us_back_to_back: mean of GEMM calls issued back to back between one event pair "
-                      "(operands left in the caches by the previous call: context, not the step)")
-    return line
-
-
-class _NoTimer:
-    def run(self, name, fn):
-        return fn()
-
-
-class _CaptureTimer(_NoTimer):
-    """Runs a step and keeps each named launch's closure."""
-
-    def __init__(self):
-        self.fns = {}
-
-    def run(self, name, fn):
-        self.fns[name] = fn
-        return fn()
 
 
 def back_to_back(step, name, reps, warmup=3):
@@ -230,6 +232,8 @@ def time_graph(step, steps, warmup, outputs):
 
 
 def time_steps(step, steps, warmup):
+    """The eager pass: `steps` steps launched from Python, each entry point between an
+    event pair.  Returns (seconds per step, timer)."""
     import torch
     timer = KernelTimer()
     for _ in range(warmup):
@@ -237,7 +241,6 @@ def time_steps(step, steps, warmup):
     torch.cuda.synchronize()
     timer.pending = []
     timer.times = {}
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         step(timer)
@@ -247,89 +250,16 @@ def time_steps(step, steps, warmup):
     return wall / steps, timer
 
 
-# ----------------------------------------------------------------------- workloads
-
-def fprop_setup():
-    import synth
-    d = synth.fprop1p5b()
-    return {"x": to_dev(d["x"]), "w": to_dev(d["w"]), "host": d}
-
-
-def _check(st, what):
-    if st != 0:
-        raise RuntimeError("%s returned status %d" % (what, st))
-
-
-def fprop_step_fn(t):
-    """The step through the C-ABI entry points with outputs allocated once, so the events
-    bracket exactly one entry point each.  Returns (step, outputs)."""
-    import torch
-    import mx_block_scaled_x128_amd as mx
-    x, w = t["x"], t["w"]
-    M, K = x.shape
-    N = w.shape[0]
-    dev = x.device
-    xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    xs = torch.empty((M, K // 128), dtype=torch.uint8, device=dev)
-    wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
-    ws = torch.empty((N // 128, K // 128), dtype=torch.uint8, device=dev)
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-
-    def step(timer):
-        stream = torch.cuda.current_stream().cuda_stream
-        _check(timer.run("quant_token_x", lambda: mx.fp8_quantize_token(
-            x.data_ptr(), mx.BF16, M, K, K, mx.ROW, mx.E4M3, xq.data_ptr(), K, xs.data_ptr(), stream)),
-            "fp8_quantize_token")
-        _check(timer.run("quant_block_w", lambda: mx.fp8_quantize_block(
-            w.data_ptr(), mx.BF16, N, K, K, mx.E4M3, wq.data_ptr(), K, ws.data_ptr(), stream)),
-            "fp8_quantize_block")
-        _check(timer.run("gemm", lambda: mx.fp8_block_scaled_gemm(
-            M, N, K, xq.data_ptr(), K, mx.E4M3, xs.data_ptr(), wq.data_ptr(), K, mx.E4M3, mx.B_NK,
-            ws.data_ptr(), mx.SCALE_BLOCK128, y.data_ptr(), N, mx.BF16, stream)), "fp8_block_scaled_gemm")
-    return step, [xq, xs, wq, ws, y]
-
-
-def cpu_baseline_fprop(host, rows):
-    """Oracle on a bounded sample: `rows` token rows of X through the token quantizer and
-    the GEMM, plus the whole weight quantizer; scaled to the full step."""
-    import oracle
-    threads = min(16, os.cpu_count() or 1)
-    x, w = host["x"], host["w"]
-    M, K = x.shape
-    N = w.shape[0]
-    rows = M if rows <= 0 else min(rows, M)
-    xs = np.ascontiguousarray(x[:rows])
-    t0 = time.perf_counter()
-    xq, xsc = oracle.quantize_rows(xs, oracle.E4M3, threads=threads)
-    t1 = time.perf_counter()
-    wq, wsc = oracle.quantize_block(w, oracle.E4M3, threads=threads)
-    t2 = time.perf_counter()
-    oracle.gemm(xq, xsc, oracle.E4M3, wq, wsc, oracle.E4M3, threads=threads)
-    t3 = time.perf_counter()
-    scale = M / float(rows)
-    t_step = (t1 - t0) * scale + (t2 - t1) + (t3 - t2) * scale
-    return {
-        "value": round(2.0 * M * N * K / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-        "kind": "oracle",
-        "sample": ("the full step" if rows == M else
-                   "%d of %d token rows through token quantization and the GEMM, full weight quantization, "
-                   "times scaled to the full step" % (rows, M))
-                  + " (oracle: fp64 C, %d host threads; %.1f s measured, %.1f s per step)" % (threads, t3 - t0, t_step),
-    }
-
-
-def gemm_traffic(workload):
-    """HBM bytes per GEMM call from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded
-    under profiles/ (scaled by a plain copy's counters), or None when the GEMM kernel's
-    source has changed since they were taken."""
-    import hashlib
-    here = os.path.dirname(os.path.abspath(__file__))
-    rec_path = os.path.join(here, "profiles", "gemm_traffic_%s.json" % workload)
-    src = os.path.join(here, "mx_block_scaled_x128_amd", "csrc", "gemm.hip")
+def recorded_traffic(workload):
+    """HBM bytes per call of the dominant kernel from the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs recorded under profiles/traffic_<workload>.json (scaled by a plain
+    copy's counters), or None when the kernel's source file has changed since."""
+    rec_path = os.path.join(HERE, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(rec_path):
         return None
     rec = json.load(open(rec_path))
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("gemm_source_sha256"):
+    src = os.path.join(HERE, "mx_block_scaled_x128_amd", "csrc", rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
         return None
     return int(rec["fetch_bytes_per_call"] + rec["write_bytes_per_call"])
 
@@ -342,50 +272,505 @@ def bytes_block(rows, cols, in_bytes):
     return rows * cols * (in_bytes + 1) + ((rows + 127) // 128) * ((cols + 127) // 128)
 
 
-def bench_fprop(args):
+def cpu_line(value, unit, threads, seconds, sample):
+    return {"value": round(value, 6), "unit": unit, "cores": threads, "host_cores": os.cpu_count(),
+            "kind": "oracle",
+            "sample": sample + " (oracle: fp64 C, %d host threads; %.1f s measured)" % (threads, seconds)}
+
+
+# ----------------------------------------------------------------------- workloads
+#
+# Each workload builds its device tensors and returns a dict:
+#   step(timer)  the whole path once, one named C-ABI call per timer.run
+#   outputs      tensors a replay must reproduce bit for bit
+#   sizes        algorithmic bytes per call of each quantizer launch
+#   flops        2*M*N*K of the GEMM (0 when the step has none)
+#   desc, config the workload description
+#   cpu(rows)    the oracle on a bounded sample of the same step -> cpu_baseline
+
+def w_dgrad7b():
     import torch
-    t = fprop_setup()
-    M, K = t["x"].shape
-    N = t["w"].shape[0]
-    step, outputs = fprop_step_fn(t)
+    import mx_block_scaled_x128_amd as mx
+    import synth
+    d = synth.dgrad7b()
+    dy, w = to_dev(d["dy"]), to_dev(d["w"])
+    M, K = dy.shape
+    N = w.shape[1]
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    gq, gs = torch.empty((M, K), **u8), torch.empty((M, K // 128), **u8)
+    wq, ws = torch.empty((K, N), **u8), torch.empty((K // 128, N // 128), **u8)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(timer):
+        stream = torch.cuda.current_stream().cuda_stream
+        _check(timer.run("quant_token_dy", lambda: mx.fp8_quantize_token(
+            dy.data_ptr(), mx.BF16, M, K, K, mx.ROW, mx.E5M2, gq.data_ptr(), K, gs.data_ptr(), stream)),
+            "fp8_quantize_token")
+        _check(timer.run("quant_block_w", lambda: mx.fp8_quantize_block(
+            w.data_ptr(), mx.BF16, K, N, N, mx.E4M3, wq.data_ptr(), N, ws.data_ptr(), stream)),
+            "fp8_quantize_block")
+        _check(timer.run("gemm", lambda: mx.fp8_block_scaled_gemm(
+            M, N, K, gq.data_ptr(), K, mx.E5M2, gs.data_ptr(), wq.data_ptr(), N, mx.E4M3, mx.B_KN,
+            ws.data_ptr(), mx.SCALE_BLOCK128, y.data_ptr(), N, mx.BF16, stream)), "fp8_block_scaled_gemm")
+
+    def cpu(rows):
+        import oracle
+        th = oracle_threads()
+        rows = M if rows == 0 else min(rows if rows > 0 else 2048, M)
+        t0 = time.perf_counter()
+        q, s = oracle.quantize_rows(np.ascontiguousarray(d["dy"][:rows]), oracle.E5M2, threads=th)
+        t1 = time.perf_counter()
+        wq_, ws_ = oracle.quantize_block(d["w"], oracle.E4M3, threads=th)
+        t2 = time.perf_counter()
+        oracle.gemm(q, s, oracle.E5M2, wq_, ws_, oracle.E4M3, oracle.B_KN, oracle.B_SCALE_BLOCK, threads=th)
+        t3 = time.perf_counter()
+        f = M / float(rows)
+        t_step = (t1 - t0) * f + (t2 - t1) + (t3 - t2) * f
+        return cpu_line(2.0 * M * N * K / t_step / 1e12, "TFLOP/s", th, t3 - t0,
+                        ("the full step" if rows == M else
+                         "%d of %d rows of dY through token quantization and the GEMM, the whole weight "
+                         "through block quantization, times scaled to the full step (%.1f s per step)"
+                         % (rows, M, t_step)))
+    return {"step": step, "outputs": [gq, gs, wq, ws, y],
+            "sizes": {"quant_token_dy": bytes_token(M, K, 2), "quant_block_w": bytes_block(K, N, 2)},
+            "flops": 2.0 * M * N * K, "M": M, "N": N, "K": K, "dtype": "fp8_e5m2 x fp8_e4m3",
+            "gemm_bytes": M * K + K * N + M * (K // 128) + (K // 128) * (N // 128) + 2 * M * N,
+            "desc": "dgrad7b: token-quantize dY 8192x18944 bf16 (1x128, E5M2) + block-quantize W 18944x3584 "
+                    "bf16 (128x128, E4M3) + block-scaled GEMM dX = dY*W, M=8192 N=3584 K=18944 (W stored "
+                    "[K][N]) bf16 out",
+            "cpu": cpu}
+
+
+def w_fprop1p5b():
+    import torch
+    import mx_block_scaled_x128_amd as mx
+    import synth
+    d = synth.fprop1p5b()
+    x, w = to_dev(d["x"]), to_dev(d["w"])
+    M, K = x.shape
+    N = w.shape[0]
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    xq, xs = torch.empty((M, K), **u8), torch.empty((M, K // 128), **u8)
+    wq, ws = torch.empty((N, K), **u8), torch.empty((N // 128, K // 128), **u8)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(timer):
+        stream = torch.cuda.current_stream().cuda_stream
+        _check(timer.run("quant_token_x", lambda: mx.fp8_quantize_token(
+            x.data_ptr(), mx.BF16, M, K, K, mx.ROW, mx.E4M3, xq.data_ptr(), K, xs.data_ptr(), stream)),
+            "fp8_quantize_token")
+        _check(timer.run("quant_block_w", lambda: mx.fp8_quantize_block(
+            w.data_ptr(), mx.BF16, N, K, K, mx.E4M3, wq.data_ptr(), K, ws.data_ptr(), stream)),
+            "fp8_quantize_block")
+        _check(timer.run("gemm", lambda: mx.fp8_block_scaled_gemm(
+            M, N, K, xq.data_ptr(), K, mx.E4M3, xs.data_ptr(), wq.data_ptr(), K, mx.E4M3, mx.B_NK,
+            ws.data_ptr(), mx.SCALE_BLOCK128, y.data_ptr(), N, mx.BF16, stream)), "fp8_block_scaled_gemm")
+
+    def cpu(rows):
+        import oracle
+        th = oracle_threads()
+        rows = M if rows <= 0 else min(rows, M)
+        t0 = time.perf_counter()
+        q, s = oracle.quantize_rows(np.ascontiguousarray(d["x"][:rows]), oracle.E4M3, threads=th)
+        t1 = time.perf_counter()
+        wq_, ws_ = oracle.quantize_block(d["w"], oracle.E4M3, threads=th)
+        t2 = time.perf_counter()
+        oracle.gemm(q, s, oracle.E4M3, wq_, ws_, oracle.E4M3, threads=th)
+        t3 = time.perf_counter()
+        f = M / float(rows)
+        t_step = (t1 - t0) * f + (t2 - t1) + (t3 - t2) * f
+        return cpu_line(2.0 * M * N * K / t_step / 1e12, "TFLOP/s", th, t3 - t0,
+                        "the full step" if rows == M else
+                        "%d of %d token rows, times scaled to the full step" % (rows, M))
+    return {"step": step, "outputs": [xq, xs, wq, ws, y],
+            "sizes": {"quant_token_x": bytes_token(M, K, 2), "quant_block_w": bytes_block(N, K, 2)},
+            "flops": 2.0 * M * N * K, "M": M, "N": N, "K": K, "dtype": "fp8_e4m3",
+            "gemm_bytes": M * K + N * K + M * (K // 128) + (N // 128) * (K // 128) + 2 * M * N,
+            "desc": "fprop1p5b: token-quantize X 4096x1536 bf16 (1x128, E4M3) + block-quantize W 8960x1536 bf16 "
+                    "(128x128, E4M3) + block-scaled GEMM M=4096 N=8960 K=1536 bf16 out",
+            "cpu": cpu}
+
+
+def w_wgrad():
+    import torch
+    import mx_block_scaled_x128_amd as mx
+    import synth
+    d = synth.wgrad()
+    x, dy = to_dev(d["x"]), to_dev(d["dy"])
+    T, C = x.shape
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    xq, xs = torch.empty((C, T), **u8), torch.empty((C, T // 128), **u8)
+    gq, gs = torch.empty((C, T), **u8), torch.empty((C, T // 128), **u8)
+    y = torch.empty((C, C), dtype=torch.float32, device="cuda")
+
+    def step(timer):
+        stream = torch.cuda.current_stream().cuda_stream
+        _check(timer.run("quant_col_x", lambda: mx.fp8_quantize_token(
+            x.data_ptr(), mx.BF16, T, C, C, mx.COL_T, mx.E4M3, xq.data_ptr(), T, xs.data_ptr(), stream)), "q")
+        _check(timer.run("quant_col_dy", lambda: mx.fp8_quantize_token(
+            dy.data_ptr(), mx.BF16, T, C, C, mx.COL_T, mx.E5M2, gq.data_ptr(), T, gs.data_ptr(), stream)), "q")
+        _check(timer.run("gemm", lambda: mx.fp8_block_scaled_gemm(
+            C, C, T, gq.data_ptr(), T, mx.E5M2, gs.data_ptr(), xq.data_ptr(), T, mx.E4M3, mx.B_NK,
+            xs.data_ptr(), mx.SCALE_ROW128, y.data_ptr(), C, mx.F32, stream)), "gemm")
+
+    def cpu(rows):
+        import oracle
+        th = oracle_threads()
+        rows = C if rows == 0 else min(rows if rows > 0 else 1024, C)
+        t0 = time.perf_counter()
+        xq_, xs_ = oracle.quantize_cols_t(d["x"], oracle.E4M3, threads=th)
+        gq_, gs_ = oracle.quantize_cols_t(d["dy"], oracle.E5M2, threads=th)
+        t1 = time.perf_counter()
+        oracle.gemm(gq_[:rows], gs_[:rows], oracle.E5M2, xq_, xs_, oracle.E4M3, oracle.B_NK, oracle.B_SCALE_ROW,
+                    threads=th)
+        t2 = time.perf_counter()
+        t_step = (t1 - t0) + (t2 - t1) * C / float(rows)
+        return cpu_line(2.0 * C * C * T / t_step / 1e12, "TFLOP/s", th, t2 - t0,
+                        "the full step" if rows == C else
+                        "both column quantizations in full, %d of %d output rows of the GEMM, times scaled to "
+                        "the full step (%.1f s per step)" % (rows, C, t_step))
+    return {"step": step, "outputs": [xq, xs, gq, gs, y],
+            "sizes": {"quant_col_x": bytes_token(T, C, 2), "quant_col_dy": bytes_token(T, C, 2)},
+            "flops": 2.0 * C * C * T, "M": C, "N": C, "K": T, "dtype": "fp8_e5m2 x fp8_e4m3",
+            "gemm_bytes": 2 * C * T + 2 * C * (T // 128) + 4 * C * C,
+            "desc": "wgrad: column-quantize X and dY 16384x4096 bf16 along tokens (E4M3 / E5M2) + GEMM "
+                    "dW = dY^T X, M=N=4096 K=16384 fp32 out",
+            "cpu": cpu}
+
+
+def w_mxfprop1p5b():
+    import torch
+    import mx_block_scaled_x128_amd as mx
+    import synth
+    d = synth.fprop1p5b()
+    x, w = to_dev(d["x"]), to_dev(d["w"])
+    M, K = x.shape
+    N = w.shape[0]
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    xq, xs = torch.empty((M, K), **u8), torch.empty((M, K // 32), **u8)
+    wq, ws = torch.empty((N, K), **u8), torch.empty((N, K // 32), **u8)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(timer):
+        stream = torch.cuda.current_stream().cuda_stream
+        _check(timer.run("mx_quant_x", lambda: mx.mx_quantize(
+            x.data_ptr(), mx.BF16, M, K, K, mx.E4M3, mx.RULE_FLOOR, xq.data_ptr(), K, xs.data_ptr(), None,
+            stream)), "mx")
+        _check(timer.run("mx_quant_w", lambda: mx.mx_quantize(
+            w.data_ptr(), mx.BF16, N, K, K, mx.E4M3, mx.RULE_FLOOR, wq.data_ptr(), K, ws.data_ptr(), None,
+            stream)), "mx")
+        _check(timer.run("gemm", lambda: mx.mx_gemm(
+            M, N, K, xq.data_ptr(), K, mx.E4M3, xs.data_ptr(), wq.data_ptr(), K, mx.E4M3, ws.data_ptr(),
+            y.data_ptr(), N, mx.BF16, stream)), "gemm")
+
+    def cpu(rows):
+        import oracle
+        th = oracle_threads()
+        rows = M if rows <= 0 else min(rows, M)
+        t0 = time.perf_counter()
+        q, s, _ = oracle.mx_quantize(np.ascontiguousarray(d["x"][:rows]), oracle.E4M3, oracle.RULE_FLOOR, threads=th)
+        t1 = time.perf_counter()
+        wq_, ws_, _ = oracle.mx_quantize(d["w"], oracle.E4M3, oracle.RULE_FLOOR, threads=th)
+        t2 = time.perf_counter()
+        oracle.mx_gemm(q, s, oracle.E4M3, wq_, ws_, oracle.E4M3, threads=th)
+        t3 = time.perf_counter()
+        f = M / float(rows)
+        t_step = (t1 - t0) * f + (t2 - t1) + (t3 - t2) * f
+        return cpu_line(2.0 * M * N * K / t_step / 1e12, "TFLOP/s", th, t3 - t0,
+                        "the full step" if rows == M else "%d of %d rows, scaled" % (rows, M))
+    return {"step": step, "outputs": [xq, xs, wq, ws, y],
+            "sizes": {"mx_quant_x": M * K * 3 + M * K // 32, "mx_quant_w": N * K * 3 + N * K // 32},
+            "flops": 2.0 * M * N * K, "M": M, "N": N, "K": K, "dtype": "fp8_e4m3",
+            "gemm_bytes": M * K + N * K + (M + N) * (K // 32) + 2 * M * N,
+            "desc": "mxfprop1p5b: MX-quantize X 4096x1536 and W 8960x1536 bf16 (32-element E4M3 blocks, OCP "
+                    "floor scales) + MX GEMM M=4096 N=8960 K=1536 bf16 out",
+            "cpu": cpu}
+
+
+def w_f32sfprop1p5b():
+    import torch
+    import mx_block_scaled_x128_amd as mx
+    import synth
+    d = synth.fprop1p5b()
+    x, w = to_dev(d["x"]), to_dev(d["w"])
+    M, K = x.shape
+    N = w.shape[0]
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    xq, xs = torch.empty((M, K), **u8), torch.empty((M, K // 128), **f32)
+    wq, ws = torch.empty((N, K), **u8), torch.empty(((N + 127) // 128, K // 128), **f32)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(timer):
+        stream = torch.cuda.current_stream().cuda_stream
+        _check(timer.run("quant_token_x_f32s", lambda: mx.fp8_quantize_token_f32s(
+            x.data_ptr(), mx.BF16, M, K, K, mx.ROW, mx.E4M3, xq.data_ptr(), K, xs.data_ptr(), stream)), "q")
+        _check(timer.run("quant_block_w_f32s", lambda: mx.fp8_quantize_block_f32s(
+            w.data_ptr(), mx.BF16, N, K, K, mx.E4M3, wq.data_ptr(), K, ws.data_ptr(), stream)), "q")
+        _check(timer.run("gemm", lambda: mx.fp8_gemm_f32s(
+            M, N, K, xq.data_ptr(), K, mx.E4M3, xs.data_ptr(), wq.data_ptr(), K, mx.E4M3, mx.B_NK,
+            ws.data_ptr(), mx.SCALE_BLOCK128, y.data_ptr(), N, mx.BF16, stream)), "gemm")
+
+    def cpu(rows):
+        import oracle
+        th = oracle_threads()
+        rows = M if rows <= 0 else min(rows, M)
+        t0 = time.perf_counter()
+        q, s = oracle.quantize_rows_f32s(np.ascontiguousarray(d["x"][:rows]), oracle.E4M3, threads=th)
+        t1 = time.perf_counter()
+        wq_, ws_ = oracle.quantize_block_f32s(d["w"], oracle.E4M3, threads=th)
+        t2 = time.perf_counter()
+        oracle.gemm_f32s(q, s, oracle.E4M3, wq_, ws_, oracle.E4M3, threads=th)
+        t3 = time.perf_counter()
+        f = M / float(rows)
+        t_step = (t1 - t0) * f + (t2 - t1) + (t3 - t2) * f
+        return cpu_line(2.0 * M * N * K / t_step / 1e12, "TFLOP/s", th, t3 - t0,
+                        "the full step" if rows == M else "%d of %d rows, scaled" % (rows, M))
+    return {"step": step, "outputs": [xq, xs, wq, ws, y],
+            "sizes": {"quant_token_x_f32s": M * K * 3 + 4 * M * (K // 128),
+                      "quant_block_w_f32s": N * K * 3 + 4 * ((N + 127) // 128) * (K // 128)},
+            "flops": 2.0 * M * N * K, "M": M, "N": N, "K": K, "dtype": "fp8_e4m3",
+            "gemm_bytes": M * K + N * K + 4 * M * (K // 128) + 4 * (N // 128) * (K // 128) + 2 * M * N,
+            "desc": "f32sfprop1p5b: token-quantize X 4096x1536 and block-quantize W 8960x1536 bf16 with fp32 "
+                    "scales (amax / 448) + GEMM over fp32-scaled operands M=4096 N=8960 K=1536 bf16 out",
+            "cpu": cpu}
+
+
+def w_dualq():
+    import torch
+    import mx_block_scaled_x128_amd as mx
+    import synth
+    hx = synth.wgrad()["x"]
+    hw = synth.dgrad7b(rows=16)["w"]
+    x, w = to_dev(hx), to_dev(hw)
+    T, C = x.shape
+    O, I = w.shape
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    xq, xs = torch.empty((T, C), **u8), torch.empty((T, C // 128), **u8)
+    xqt, xst = torch.empty((C, T), **u8), torch.empty((C, T // 128), **u8)
+    wq, ws = torch.empty((O, I), **u8), torch.empty(((O + 127) // 128, I // 128), **u8)
+    wqt, wst = torch.empty((I, O), **u8), torch.empty((I // 128, (O + 127) // 128), **u8)
+
+    def step(timer):
+        stream = torch.cuda.current_stream().cuda_stream
+        _check(timer.run("token_dual_x", lambda: mx.fp8_quantize_token_dual(
+            x.data_ptr(), mx.BF16, T, C, C, mx.E4M3, xq.data_ptr(), C, xs.data_ptr(), xqt.data_ptr(), T,
+            xst.data_ptr(), stream)), "dual")
+        _check(timer.run("block_dual_w", lambda: mx.fp8_quantize_block_dual(
+            w.data_ptr(), mx.BF16, O, I, I, mx.E4M3, wq.data_ptr(), I, ws.data_ptr(), wqt.data_ptr(), O,
+            wst.data_ptr(), stream)), "dual")
+    sizes = {"token_dual_x": T * C * 4 + 2 * T * C // 128,
+             "block_dual_w": O * I * 4 + 2 * ((O + 127) // 128) * (I // 128)}
+
+    def cpu(rows):
+        import oracle
+        th = oracle_threads()
+        t0 = time.perf_counter()
+        oracle.quantize_rows(hx, oracle.E4M3, threads=th)
+        oracle.quantize_cols_t(hx, oracle.E4M3, threads=th)
+        q, _ = oracle.quantize_block(hw, oracle.E4M3, threads=th)
+        np.ascontiguousarray(q.T)
+        t1 = time.perf_counter()
+        return cpu_line(sum(sizes.values()) / (t1 - t0) / 1e9, "GB/s", th, t1 - t0,
+                        "the full step (row and transposed-column codes of X, block codes of W and their "
+                        "transpose)")
+    return {"step": step, "outputs": [xq, xs, xqt, xst, wq, ws, wqt, wst], "sizes": sizes, "flops": 0.0,
+            "M": 0, "N": 0, "K": 0, "dtype": "fp8_e4m3",
+            "desc": "dualq: X 16384x4096 bf16 -> 1x128 row codes + 128-token column codes (transposed), one read; "
+                    "W 18944x3584 bf16 -> 128x128 block codes + their transpose",
+            "cpu": cpu}
+
+
+def w_gaussws7b():
+    import torch
+    import mx_block_scaled_x128_amd as mx
+    import synth
+    wf = synth.bf16_bits_to_f32(synth.dgrad7b(rows=16)["w"]).astype(np.float32)
+    R, C = wf.shape
+    bt_np = np.random.default_rng(10).integers(4, 9, (-(-R // 32), -(-C // 32))).astype(np.int8)
+    w = to_dev(wf)
+    bt = torch.from_numpy(bt_np).cuda()
+    w_hat = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+
+    def step(timer):
+        stream = torch.cuda.current_stream().cuda_stream
+        _check(timer.run("gaussws", lambda: mx.gaussws_sample(
+            w.data_ptr(), mx.F32, R, C, C, bt.data_ptr(), 2025, 7, w_hat.data_ptr(), C, stream)), "gws")
+    sizes = {"gaussws": R * C * 6 + bt_np.size}
+
+    def cpu(rows):
+        import oracle
+        th = oracle_threads()
+        t0 = time.perf_counter()
+        oracle.gaussws(wf, bt_np, 2025, 7, threads=th)
+        t1 = time.perf_counter()
+        return cpu_line(sizes["gaussws"] / (t1 - t0) / 1e9, "GB/s", th, t1 - t0, "the full step")
+    return {"step": step, "outputs": [w_hat], "sizes": sizes, "flops": 0.0, "M": 0, "N": 0, "K": 0,
+            "dtype": "bf16",
+            "desc": "gaussws7b: GaussWS sampled weight of W 18944x3584 fp32 master weights (32x32 blocks, int8 "
+                    "bitwidths 4..8, Philox4x64-10 rounded-normal noise) -> bf16",
+            "cpu": cpu}
+
+
+E4M3_TOP = 0x7E
+
+
+def mx_clamp_stats(q, cnt, clustered_rows):
+    """Clamp statistics of one tensor's MX codes and counts (numpy), split into the
+    clustered rows [0, clustered_rows) and the others: per block, the fraction of its
+    32 values whose scaled magnitude exceeded the largest code (strict clamp); the
+    fraction of values on the top code; the fraction of blocks whose 32 codes are all
+    one code."""
+    out = {}
+    for part, sl in (("clustered", slice(0, clustered_rows)), ("normal", slice(clustered_rows, None))):
+        c = cnt[sl].astype(np.int64)
+        qq = q[sl]
+        blocks = qq.reshape(qq.shape[0], -1, 32)
+        out[part] = {
+            "values": int(qq.size), "blocks": int(c.size), "clamped": int(c.sum()),
+            "blocks_with_clamp": int((c > 0).sum()), "max_clamped_in_block": int(c.max()),
+            "top_code": int(((qq & 0x7F) == E4M3_TOP).sum()),
+            "single_code_blocks": int((blocks == blocks[:, :, :1]).all(axis=2).sum())}
+    return out
+
+
+def w_mxstress():
+    import torch
+    import mx_block_scaled_x128_amd as mx
+    import synth
+    ntens = 64
+    hosts = [synth.mxstress_tensor(j) for j in range(ntens)]
+    xs_ = [to_dev(h) for h in hosts]
+    R, C = xs_[0].shape
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    q, sc, cn = torch.empty((R, C), **u8), torch.empty((R, C // 32), **u8), torch.empty((R, C // 32), **u8)
+
+    def step(timer):
+        stream = torch.cuda.current_stream().cuda_stream
+        for j in range(ntens):
+            _check(timer.run("mx_quant", lambda: mx.mx_quantize(
+                xs_[j].data_ptr(), mx.F32, R, C, C, mx.E4M3, mx.RULE_FLOOR, q.data_ptr(), C, sc.data_ptr(),
+                cn.data_ptr(), stream)), "mx")
+    sizes = {"mx_quant": R * C * 5 + 2 * R * (C // 32)}
+
+    def device_stats():
+        """Clamp statistics of every tensor from the device's codes and counts."""
+        per = []
+        for j in range(ntens):
+            qd, _, cd = mx.quantize_mx(xs_[j], mx.E4M3, mx.RULE_FLOOR, counts=True)
+            per.append(mx_clamp_stats(qd.cpu().numpy(), cd.cpu().numpy(), R // 2))
+        return per
+
+    def cpu(rows):
+        import oracle
+        th = oracle_threads()
+        t0 = time.perf_counter()
+        ref = []
+        for h in hosts:
+            qr, _, cr = oracle.mx_quantize(h, oracle.E4M3, oracle.RULE_FLOOR, threads=th)
+            ref.append((qr, cr))
+        t1 = time.perf_counter()
+        line = cpu_line(sizes["mx_quant"] * ntens / (t1 - t0) / 1e9, "GB/s", th, t1 - t0,
+                        "all 64 tensors (the full step)")
+        return line, [mx_clamp_stats(qr, cr, R // 2) for qr, cr in ref]
+    return {"step": step, "outputs": [q, sc, cn], "sizes": sizes, "flops": 0.0, "M": 0, "N": 0, "K": 0,
+            "dtype": "fp8_e4m3", "calls": {"mx_quant": ntens}, "device_stats": device_stats,
+            "desc": "mxstress: 64 tensors 4096x4096 fp32 (rows [0,2048) 1 + N(0,1e-3), rows [2048,4096) N(0,1)), "
+                    "MX 32-element E4M3 blocks, OCP floor scales, clamp counts",
+            "cpu": cpu}
+
+
+def summarize_stats(per):
+    """Totals over tensors, as fractions: values clamped, blocks with a clamp, the
+    largest per-block clamped fraction, values on the top code, single-code blocks."""
+    out = {}
+    for part in ("normal", "clustered"):
+        tot = {k: sum(p[part][k] for p in per) for k in ("values", "blocks", "clamped", "blocks_with_clamp",
+                                                        "top_code", "single_code_blocks")}
+        out[part] = {
+            "clamped_fraction": tot["clamped"] / tot["values"],
+            "mean_clamped_fraction_per_block": tot["clamped"] / (32.0 * tot["blocks"]),
+            "max_clamped_fraction_in_a_block": max(p[part]["max_clamped_in_block"] for p in per) / 32.0,
+            "blocks_with_a_clamp": tot["blocks_with_clamp"] / tot["blocks"],
+            "top_code_fraction": tot["top_code"] / tot["values"],
+            "single_code_block_fraction": tot["single_code_blocks"] / tot["blocks"],
+            "counts": tot}
+    return out
+
+
+SETUP = {"dgrad7b": w_dgrad7b, "fprop1p5b": w_fprop1p5b, "wgrad": w_wgrad, "mxfprop1p5b": w_mxfprop1p5b,
+         "f32sfprop1p5b": w_f32sfprop1p5b, "dualq": w_dualq, "gaussws7b": w_gaussws7b, "mxstress": w_mxstress}
+
+
+def bench_workload(args):
+    wl = SETUP[args.workload]()
+    step, sizes, flops = wl["step"], wl["sizes"], wl["flops"]
+    calls = wl.get("calls", {})
     per_step_eager, timer = time_steps(step, args.steps, args.warmup)
-    per_step, per_graph = time_graph(step, args.steps, args.warmup, outputs)
-    flops = 2.0 * M * N * K
-    g = timer.mean("gemm")
-    gb = back_to_back(step, "gemm", max(20, args.steps))
-    qx = timer.mean("quant_token_x")
-    qw = timer.mean("quant_block_w")
-    bx = bytes_token(M, K, 2)
-    bw = bytes_block(N, K, 2)
-    gemm_tflops = flops / g / 1e12
+    per_step, per_graph = time_graph(step, args.steps, args.warmup, wl["outputs"])
+    kern = {}
+    for name, b in sizes.items():
+        t = timer.mean(name)
+        kern[name] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
+                      "frac_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4), "bytes": b}
+    traffic = recorded_traffic(args.workload)
+    if flops:
+        g = timer.mean("gemm")
+        gb = back_to_back(step, "gemm", max(20, args.steps))
+        kern["gemm"] = {"us": round(g * 1e6, 2), "TFLOP/s": round(flops / g / 1e12, 1),
+                        "frac_fp8_peak": round(flops / g / 1e12 / FP8_PEAK_TFLOPS, 4), "flops": flops,
+                        "us_back_to_back": round(gb * 1e6, 2)}
+        value, unit = flops / per_step / 1e12, "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": round(flops / g / 1e12, 2), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(flops / g / 1e12 / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
+                "kernel": "gemm",
+                "traffic_note": "HBM bytes per GEMM call (FETCH_SIZE + WRITE_SIZE, copy-calibrated; "
+                                "profiles/traffic_%s.json); algorithmic bytes %d" % (args.workload, wl["gemm_bytes"])}
+    else:
+        tot = sum(b * calls.get(name, 1) for name, b in sizes.items())
+        value, unit = tot / per_step / 1e9, "GB/s"
+        dom = max(sizes, key=lambda k: kern[k]["us"])
+        roof = {"bound": "hbm", "achieved": kern[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": kern[dom]["frac_hbm_peak"], "traffic": traffic, "kernel": dom,
+                "traffic_note": "HBM bytes per call of %s (FETCH_SIZE + WRITE_SIZE, copy-calibrated; "
+                                "profiles/traffic_%s.json); algorithmic bytes %d" % (dom, args.workload, sizes[dom])}
+    config = {"workload": wl["desc"]}
+    if flops:
+        config.update({"M": wl["M"], "N": wl["N"], "K": wl["K"]})
     line = {
-        "metric": METRIC, "value": round(flops / per_step / 1e12, 3), "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(per_step * 1e3, 4),
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(per_step * 1e3, 4),
         "ms_per_step_eager": round(per_step_eager * 1e3, 4), "steps_per_graph": per_graph,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
-        "data": "synthetic (seeded numpy PCG64; bf16 inputs resident in HBM before timing)",
-        "config": {"workload": "fprop1p5b: token-quantize X 4096x1536 bf16 (1x128, E4M3) + block-quantize "
-                               "W 8960x1536 bf16 (128x128, E4M3) + block-scaled GEMM M=4096 N=8960 K=1536 "
-                               "bf16 out", "M": M, "N": N, "K": K, "global_batch": M, "parallelism": "single GPU"},
-        "kernels": {
-            "quant_token_x": {"us": round(qx * 1e6, 2), "GB/s": round(bx / qx / 1e9, 1),
-                              "frac_hbm_peak": round(bx / qx / 1e9 / HBM_PEAK_GBS, 4), "bytes": bx},
-            "quant_block_w": {"us": round(qw * 1e6, 2), "GB/s": round(bw / qw / 1e9, 1),
-                              "frac_hbm_peak": round(bw / qw / 1e9 / HBM_PEAK_GBS, 4), "bytes": bw},
-            "gemm": {"us": round(g * 1e6, 2), "TFLOP/s": round(gemm_tflops, 1),
-                     "frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "flops": flops,
-                     "us_back_to_back": round(gb * 1e6, 2)},
-        },
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": FP8_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
-                     "traffic": gemm_traffic("fprop1p5b"),
-                     "traffic_note": "HBM bytes per GEMM call (FETCH_SIZE + WRITE_SIZE, copy-calibrated; "
-                                     "profiles/gemm_traffic_fprop1p5b.json); algorithmic bytes %d"
-                                     % (M * K + N * K + M * (K // 128) + ((N + 127) // 128) * (K // 128)
-                                        + 2 * M * N)},
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl["dtype"],
+        "data": "synthetic (seeded numpy PCG64; inputs resident in HBM before timing)",
+        "config": config, "kernels": kern, "roofline": roof,
     }
-    add_context(line, step, timer)
-    line["cpu_baseline"] = None if args.no_cpu else cpu_baseline_fprop(t["host"], args.cpu_rows)
+    if args.workload != "mxstress":  # 64 launches per step: the scrubbed pass would take long
+        per, device = context_measurements(step, timer)
+        for name, d in per.items():
+            if name in line["kernels"]:
+                line["kernels"][name].update(d)
+        line["device"] = device
+    line["timing"] = ("value: replays of a graph of steps_per_graph whole steps between synchronisations; "
+                      "kernels.us: mean of event-bracketed eager calls inside the step, on the stream they run on "
+                      "(us_median: median); us_cold_median: each call after a 512 MiB scrub write, medians of 10; "
+                      "roofline.achieved: from kernels.<kernel>.us; gemm.us_back_to_back: mean of GEMM calls "
+                      "issued back to back between one event pair (operands left in the caches by the previous "
+                      "call: context, not the step)")
+    cpu_stats = None
+    if args.no_cpu:
+        line["cpu_baseline"] = None
+    elif args.workload == "mxstress":
+        line["cpu_baseline"], cpu_stats = wl["cpu"](args.cpu_rows)
+    else:
+        line["cpu_baseline"] = wl["cpu"](args.cpu_rows)
+    if "device_stats" in wl:
+        per = wl["device_stats"]()
+        line["clamp_stats"] = summarize_stats(per)
+        line["clamp_stats"]["oracle_check"] = (
+            "not run (--no-cpu)" if cpu_stats is None else
+            "the oracle's codes and counts give the same statistics for %d of %d tensors"
+            % (sum(a == b for a, b in zip(per, cpu_stats)), len(per)))
     return line
 
 
@@ -459,214 +844,6 @@ def bench_copy(args):
             "cpu_baseline": None}
 
 
-def bench_other(args):
-    """Per-kernel figures for the larger workloads (same JSON shape, kernels block filled).
-    Outputs are allocated once; events bracket one C-ABI launch each."""
-    import torch
-    import mx_block_scaled_x128_amd as mx
-    import synth
-    u8 = dict(dtype=torch.uint8, device="cuda")
-
-    def cur():
-        return torch.cuda.current_stream().cuda_stream
-    kern = {}
-    if args.workload == "dgrad7b":
-        d = synth.dgrad7b()
-        dy, w = to_dev(d["dy"]), to_dev(d["w"])
-        del d
-        M, K = dy.shape
-        N = w.shape[1]
-        gq, gs = torch.empty((M, K), **u8), torch.empty((M, K // 128), **u8)
-        wq, ws = torch.empty((K, N), **u8), torch.empty((K // 128, N // 128), **u8)
-        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-
-        def step(timer):
-            stream = cur()
-            _check(timer.run("quant_token_dy", lambda: mx.fp8_quantize_token(
-                dy.data_ptr(), mx.BF16, M, K, K, mx.ROW, mx.E5M2, gq.data_ptr(), K, gs.data_ptr(), stream)), "q")
-            _check(timer.run("quant_block_w", lambda: mx.fp8_quantize_block(
-                w.data_ptr(), mx.BF16, K, N, N, mx.E4M3, wq.data_ptr(), N, ws.data_ptr(), stream)), "q")
-            _check(timer.run("gemm", lambda: mx.fp8_block_scaled_gemm(
-                M, N, K, gq.data_ptr(), K, mx.E5M2, gs.data_ptr(), wq.data_ptr(), N, mx.E4M3, mx.B_KN,
-                ws.data_ptr(), mx.SCALE_BLOCK128, y.data_ptr(), N, mx.BF16, stream)), "gemm")
-        sizes = {"quant_token_dy": bytes_token(M, K, 2), "quant_block_w": bytes_block(K, N, 2)}
-        outputs = [gq, gs, wq, ws, y]
-        flops = 2.0 * M * N * K
-        desc = "dgrad7b: token-quantize dY 8192x18944 bf16 (E5M2) + block-quantize W 18944x3584 (E4M3) + GEMM " \
-               "M=8192 N=3584 K=18944 (B stored [K][N]) bf16 out"
-    elif args.workload == "wgrad":
-        d = synth.wgrad()
-        x, dy = to_dev(d["x"]), to_dev(d["dy"])
-        del d
-        T, C = x.shape
-        xq, xs = torch.empty((C, T), **u8), torch.empty((C, T // 128), **u8)
-        gq, gs = torch.empty((C, T), **u8), torch.empty((C, T // 128), **u8)
-        y = torch.empty((C, C), dtype=torch.float32, device="cuda")
-
-        def step(timer):
-            stream = cur()
-            _check(timer.run("quant_col_x", lambda: mx.fp8_quantize_token(
-                x.data_ptr(), mx.BF16, T, C, C, mx.COL_T, mx.E4M3, xq.data_ptr(), T, xs.data_ptr(), stream)), "q")
-            _check(timer.run("quant_col_dy", lambda: mx.fp8_quantize_token(
-                dy.data_ptr(), mx.BF16, T, C, C, mx.COL_T, mx.E5M2, gq.data_ptr(), T, gs.data_ptr(), stream)), "q")
-            _check(timer.run("gemm", lambda: mx.fp8_block_scaled_gemm(
-                C, C, T, gq.data_ptr(), T, mx.E5M2, gs.data_ptr(), xq.data_ptr(), T, mx.E4M3, mx.B_NK,
-                xs.data_ptr(), mx.SCALE_ROW128, y.data_ptr(), C, mx.F32, stream)), "gemm")
-        sizes = {"quant_col_x": bytes_token(T, C, 2), "quant_col_dy": bytes_token(T, C, 2)}
-        outputs = [xq, xs, gq, gs, y]
-        M = N = C
-        K = T
-        flops = 2.0 * M * N * K
-        desc = "wgrad: column-quantize X and dY 16384x4096 bf16 along tokens (E4M3 / E5M2) + GEMM M=N=4096 " \
-               "K=16384 fp32 out"
-    elif args.workload == "mxfprop1p5b":
-        d = synth.fprop1p5b()
-        x, w = to_dev(d["x"]), to_dev(d["w"])
-        del d
-        M, K = x.shape
-        N = w.shape[0]
-        xq, xs = torch.empty((M, K), **u8), torch.empty((M, K // 32), **u8)
-        wq, ws = torch.empty((N, K), **u8), torch.empty((N, K // 32), **u8)
-        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-
-        def step(timer):
-            stream = cur()
-            _check(timer.run("mx_quant_x", lambda: mx.mx_quantize(
-                x.data_ptr(), mx.BF16, M, K, K, mx.E4M3, mx.RULE_FLOOR, xq.data_ptr(), K, xs.data_ptr(), None,
-                stream)), "mx")
-            _check(timer.run("mx_quant_w", lambda: mx.mx_quantize(
-                w.data_ptr(), mx.BF16, N, K, K, mx.E4M3, mx.RULE_FLOOR, wq.data_ptr(), K, ws.data_ptr(), None,
-                stream)), "mx")
-            _check(timer.run("gemm", lambda: mx.mx_gemm(
-                M, N, K, xq.data_ptr(), K, mx.E4M3, xs.data_ptr(), wq.data_ptr(), K, mx.E4M3, ws.data_ptr(),
-                y.data_ptr(), N, mx.BF16, stream)), "gemm")
-        sizes = {"mx_quant_x": M * K * 3 + M * K // 32, "mx_quant_w": N * K * 3 + N * K // 32}
-        outputs = [xq, xs, wq, ws, y]
-        flops = 2.0 * M * N * K
-        desc = "mxfprop1p5b: MX-quantize X 4096x1536 and W 8960x1536 bf16 (32-element E4M3 blocks, OCP floor " \
-               "scales) + MX GEMM M=4096 N=8960 K=1536 bf16 out"
-    elif args.workload == "f32sfprop1p5b":
-        d = synth.fprop1p5b()
-        x, w = to_dev(d["x"]), to_dev(d["w"])
-        del d
-        M, K = x.shape
-        N = w.shape[0]
-        f32 = dict(dtype=torch.float32, device="cuda")
-        xq, xs = torch.empty((M, K), **u8), torch.empty((M, K // 128), **f32)
-        wq, ws = torch.empty((N, K), **u8), torch.empty(((N + 127) // 128, K // 128), **f32)
-        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-
-        def step(timer):
-            stream = cur()
-            _check(timer.run("quant_token_x_f32s", lambda: mx.fp8_quantize_token_f32s(
-                x.data_ptr(), mx.BF16, M, K, K, mx.ROW, mx.E4M3, xq.data_ptr(), K, xs.data_ptr(), stream)), "q")
-            _check(timer.run("quant_block_w_f32s", lambda: mx.fp8_quantize_block_f32s(
-                w.data_ptr(), mx.BF16, N, K, K, mx.E4M3, wq.data_ptr(), K, ws.data_ptr(), stream)), "q")
-            _check(timer.run("gemm", lambda: mx.fp8_gemm_f32s(
-                M, N, K, xq.data_ptr(), K, mx.E4M3, xs.data_ptr(), wq.data_ptr(), K, mx.E4M3, mx.B_NK,
-                ws.data_ptr(), mx.SCALE_BLOCK128, y.data_ptr(), N, mx.BF16, stream)), "gemm")
-        sizes = {"quant_token_x_f32s": M * K * 3 + 4 * M * (K // 128),
-                 "quant_block_w_f32s": N * K * 3 + 4 * ((N + 127) // 128) * (K // 128)}
-        outputs = [xq, xs, wq, ws, y]
-        flops = 2.0 * M * N * K
-        desc = "f32sfprop1p5b: token-quantize X 4096x1536 and block-quantize W 8960x1536 bf16 with fp32 scales " \
-               "(amax / 448) + GEMM over fp32-scaled operands M=4096 N=8960 K=1536 bf16 out"
-    elif args.workload == "gaussws7b":
-        wf = synth.bf16_bits_to_f32(synth.dgrad7b(rows=16)["w"]).astype(np.float32)
-        R, C = wf.shape
-        bt_np = np.random.default_rng(10).integers(4, 9, (-(-R // 32), -(-C // 32))).astype(np.int8)
-        w = to_dev(wf)
-        bt = torch.from_numpy(bt_np).cuda()
-        del wf
-        w_hat = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
-        counter = [0]
-
-        def step(timer):
-            stream = cur()
-            _check(timer.run("gaussws", lambda: mx.gaussws_sample(
-                w.data_ptr(), mx.F32, R, C, C, bt.data_ptr(), 2025, 7, w_hat.data_ptr(), C, stream)), "gws")
-        sizes = {"gaussws": R * C * 6 + bt_np.size}
-        outputs = [w_hat]
-        flops = 0.0
-        M = N = K = 0
-        desc = "gaussws7b: GaussWS sampled weight of W 18944x3584 fp32 master weights (32x32 blocks, int8 " \
-               "bitwidths 4..8, Philox4x64-10 rounded-normal noise) -> bf16"
-    elif args.workload == "dualq":
-        x = to_dev(synth.wgrad()["x"])
-        w = to_dev(synth.dgrad7b(rows=16)["w"])
-        T, C = x.shape
-        O, I = w.shape
-        xq, xs = torch.empty((T, C), **u8), torch.empty((T, C // 128), **u8)
-        xqt, xst = torch.empty((C, T), **u8), torch.empty((C, T // 128), **u8)
-        wq, ws = torch.empty((O, I), **u8), torch.empty(((O + 127) // 128, I // 128), **u8)
-        wqt, wst = torch.empty((I, O), **u8), torch.empty((I // 128, (O + 127) // 128), **u8)
-
-        def step(timer):
-            stream = cur()
-            _check(timer.run("token_dual_x", lambda: mx.fp8_quantize_token_dual(
-                x.data_ptr(), mx.BF16, T, C, C, mx.E4M3, xq.data_ptr(), C, xs.data_ptr(), xqt.data_ptr(), T,
-                xst.data_ptr(), stream)), "dual")
-            _check(timer.run("block_dual_w", lambda: mx.fp8_quantize_block_dual(
-                w.data_ptr(), mx.BF16, O, I, I, mx.E4M3, wq.data_ptr(), I, ws.data_ptr(), wqt.data_ptr(), O,
-                wst.data_ptr(), stream)), "dual")
-        sizes = {"token_dual_x": T * C * 4 + 2 * T * C // 128,
-                 "block_dual_w": O * I * 4 + 2 * ((O + 127) // 128) * (I // 128)}
-        outputs = [xq, xs, xqt, xst, wq, ws, wqt, wst]
-        flops = 0.0
-        M = N = K = 0
-        desc = "dualq: X 16384x4096 bf16 -> 1x128 row codes + 128-token column codes (transposed), one read; " \
-               "W 18944x3584 bf16 -> 128x128 block codes + their transpose"
-    else:
-        xs_ = [to_dev(synth.mxstress_tensor(j)) for j in range(64)]
-        R, C = xs_[0].shape
-        q, sc, cn = torch.empty((R, C), **u8), torch.empty((R, C // 32), **u8), torch.empty((R, C // 32), **u8)
-
-        def step(timer):
-            stream = cur()
-            for j in range(64):
-                _check(timer.run("mx_quant", lambda: mx.mx_quantize(
-                    xs_[j].data_ptr(), mx.F32, R, C, C, mx.E4M3, mx.RULE_FLOOR, q.data_ptr(), C, sc.data_ptr(),
-                    cn.data_ptr(), stream)), "mx")
-        sizes = {"mx_quant": R * C * 5 + 2 * R * (C // 32)}
-        outputs = [q, sc, cn]
-        flops = 0.0
-        M = N = K = 0
-        desc = "mxstress: 64 tensors 4096x4096 fp32, MX 32-element E4M3 blocks, OCP floor scales, clamp counts"
-    per_step_eager, timer = time_steps(step, args.steps, args.warmup)
-    per_step, per_graph = time_graph(step, args.steps, args.warmup, outputs)
-    for name, b in sizes.items():
-        t = timer.mean(name)
-        kern[name] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
-                      "frac_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4), "bytes": b}
-    if flops:
-        g = timer.mean("gemm")
-        gb = back_to_back(step, "gemm", max(20, args.steps))
-        kern["gemm"] = {"us": round(g * 1e6, 2), "TFLOP/s": round(flops / g / 1e12, 1),
-                        "frac_fp8_peak": round(flops / g / 1e12 / FP8_PEAK_TFLOPS, 4), "flops": flops,
-                        "us_back_to_back": round(gb * 1e6, 2)}
-        value, unit = flops / per_step / 1e12, "TFLOP/s"
-        roof = {"bound": "mfma", "achieved": round(flops / g / 1e12, 2), "peak": FP8_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(flops / g / 1e12 / FP8_PEAK_TFLOPS, 4), "traffic": None}
-    else:
-        tot = sum(sizes.values()) * (64 if args.workload == "mxstress" else 1)
-        value, unit = tot / per_step / 1e9, "GB/s"
-        dom = max(sizes, key=lambda k: kern[k]["us"])
-        roof = {"bound": "hbm", "achieved": kern[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": kern[dom]["frac_hbm_peak"], "traffic": None, "kernel": dom}
-    line = {
-        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(per_step * 1e3, 4),
-        "ms_per_step_eager": round(per_step_eager * 1e3, 4), "steps_per_graph": per_graph,
-        "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8", "data": "synthetic (seeded numpy PCG64)",
-        "config": {"workload": desc, "M": M, "N": N, "K": K}, "kernels": kern, "roofline": roof,
-        "cpu_baseline": None,
-    }
-    if args.workload != "mxstress":  # 64 launches per step: the scrubbed pass would take long
-        add_context(line, step, timer)
-    return line
-
-
 def main():
     args = parse()
     if args.gpus != 1:
@@ -679,14 +856,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    if args.workload == "fprop1p5b":
-        line = bench_fprop(args)
-    elif args.workload == "copy":
+    if args.workload == "copy":
         line = bench_copy(args)
     elif args.workload == "gemmsweep":
         line = bench_gemm_sweep(args)
     else:
-        line = bench_other(args)
+        line = bench_workload(args)
     print(json.dumps(line), flush=True)
 
 

@@ -160,6 +160,13 @@ def mxfp8_version():
 
 
 # ------------------------------------------------------------------ tensor helpers
+#
+# The C entry points take raw pointers and cannot see a tensor's extent, so
+# the tensor conveniences below check every tensor before passing its
+# pointer: dtype, the exact shape the header documents for it, unit column
+# stride (dense for scale, count and bitwidth arrays), and that all tensors
+# live on the current CUDA device, whose current stream (or the given one)
+# the work goes to.  A mismatch raises ValueError before any call.
 
 def _torch():
     import torch
@@ -171,9 +178,64 @@ def _check(status, where):
         raise MxFp8Error(status, where)
 
 
-def _stream(stream):
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _code_dtypes():
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
+    return tuple(d for d in (torch.uint8, getattr(torch, "float8_e4m3fn", None),
+                             getattr(torch, "float8_e5m2", None)) if d is not None)
+
+
+def _scale_dtypes():
+    torch = _torch()
+    return tuple(d for d in (torch.uint8, getattr(torch, "float8_e8m0fnu", None)) if d is not None)
+
+
+def _is_tensor(t):
+    return isinstance(t, _torch().Tensor)
+
+
+def _matrix(t, name, dtypes, shape):
+    """A 2-D tensor of one of `dtypes`, of exactly `shape`, with unit column stride
+    (rows may be padded: the row stride is passed as the leading dimension)."""
+    _require(_is_tensor(t), "%s must be a torch tensor" % name)
+    _require(t.dim() == 2, "%s must be 2-D, got %d-D" % (name, t.dim()))
+    _require(t.dtype in dtypes, "%s must have dtype %s, got %s"
+             % (name, " or ".join(str(d) for d in dtypes), t.dtype))
+    _require(tuple(t.shape) == tuple(shape), "%s must have shape %s, got %s"
+             % (name, tuple(shape), tuple(t.shape)))
+    _require(t.shape[1] <= 1 or t.stride(1) == 1, "%s must have unit column stride" % name)
+    _require(t.shape[0] <= 1 or t.stride(0) >= t.shape[1], "%s rows must not overlap" % name)
+
+
+def _dense(t, name, dtypes, shape):
+    """A contiguous tensor of one of `dtypes` and exactly `shape` (scale, count and
+    bitwidth arrays carry no leading dimension)."""
+    _matrix(t, name, dtypes, shape)
+    _require(t.is_contiguous(), "%s must be contiguous (dense %s)" % (name, tuple(shape)))
+
+
+def _device_of(named):
+    """All tensors on one CUDA device, which must be the current device."""
+    torch = _torch()
+    dev = None
+    for name, t in named:
+        _require(t.is_cuda, "%s must be a CUDA tensor, got device %s" % (name, t.device))
+        if dev is None:
+            dev = t.device
+        _require(t.device == dev, "%s is on %s but %s is on %s" % (name, t.device, named[0][0], dev))
+    cur = torch.cuda.current_device()
+    _require(dev.index == cur, "tensors are on %s but the current device is cuda:%d" % (dev, cur))
+    return dev
+
+
+def _stream(stream, dev):
+    torch = _torch()
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    _require(s.device == dev, "stream is on %s but the tensors are on %s" % (s.device, dev))
     return s.cuda_stream
 
 
@@ -183,17 +245,27 @@ def _in_dtype(t):
         return F32
     if t.dtype == torch.bfloat16:
         return BF16
-    raise TypeError("input must be float32 or bfloat16, got %s" % t.dtype)
+    raise ValueError("input must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _input(x, name):
+    """A float32 / bfloat16 2-D input with unit column stride; returns (rows, cols)."""
+    torch = _torch()
+    _require(_is_tensor(x) and x.dim() == 2, "%s must be a 2-D torch tensor" % name)
+    _matrix(x, name, (torch.float32, torch.bfloat16), tuple(x.shape))
+    return x.shape
 
 
 def _ld(t):
-    if t.dim() != 2 or t.stride(1) != 1:
-        raise ValueError("expected a 2-D tensor with unit column stride")
-    return t.stride(0)
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
 
 
 def _pad16(n):
     return (n + 15) // 16 * 16
+
+
+def _cdiv(a, b):
+    return (a + b - 1) // b
 
 
 def _codes(rows, cols, device):
@@ -203,19 +275,40 @@ def _codes(rows, cols, device):
     return buf[:, :cols]
 
 
+def _check_out(out, out_dtype, M, N):
+    """The GEMM output, if given: [M][N], float32 or bfloat16; otherwise out_dtype."""
+    torch = _torch()
+    if out is None:
+        _require(out_dtype in (None, torch.float32, torch.bfloat16),
+                 "out_dtype must be torch.float32 or torch.bfloat16, got %s" % (out_dtype,))
+    else:
+        _matrix(out, "out", (torch.float32, torch.bfloat16), (M, N))
+
+
+def _out_matrix(out, out_dtype, M, N, device):
+    """`out` (already checked), or a new [M][N] output with a 16-element row pitch."""
+    torch = _torch()
+    if out is not None:
+        return out
+    dt = torch.bfloat16 if out_dtype == torch.bfloat16 else torch.float32
+    buf = torch.empty((M, _pad16(max(N, 1))), dtype=dt, device=device)
+    return buf[:, :N]
+
+
 def quantize_token(x, fmt=E4M3, axis=ROW, stream=None):
     """Token-wise 1x128 quantization.  ROW: (q [rows][cols], scales [rows][ceil(cols/128)]).
     COL_T: (qt [cols][rows], scales [cols][ceil(rows/128)])."""
     torch = _torch()
-    rows, cols = x.shape
+    rows, cols = _input(x, "x")
+    dev = _device_of([("x", x)])
     if axis == ROW:
-        q = _codes(rows, cols, x.device)
-        s = torch.empty((rows, (cols + 127) // 128), dtype=torch.uint8, device=x.device)
+        q = _codes(rows, cols, dev)
+        s = torch.empty((rows, _cdiv(cols, 128)), dtype=torch.uint8, device=dev)
     else:
-        q = _codes(cols, rows, x.device)
-        s = torch.empty((cols, (rows + 127) // 128), dtype=torch.uint8, device=x.device)
+        q = _codes(cols, rows, dev)
+        s = torch.empty((cols, _cdiv(rows, 128)), dtype=torch.uint8, device=dev)
     st = fp8_quantize_token(x.data_ptr(), _in_dtype(x), rows, cols, _ld(x), axis, fmt, q.data_ptr(), _ld(q),
-                            s.data_ptr(), _stream(stream))
+                            s.data_ptr(), _stream(stream, dev))
     _check(st, "fp8_quantize_token")
     return q, s
 
@@ -223,11 +316,12 @@ def quantize_token(x, fmt=E4M3, axis=ROW, stream=None):
 def quantize_block(w, fmt=E4M3, stream=None):
     """128x128 block quantization: (q [rows][cols], scales [ceil(rows/128)][ceil(cols/128)])."""
     torch = _torch()
-    rows, cols = w.shape
-    q = _codes(rows, cols, w.device)
-    s = torch.empty(((rows + 127) // 128, (cols + 127) // 128), dtype=torch.uint8, device=w.device)
+    rows, cols = _input(w, "w")
+    dev = _device_of([("w", w)])
+    q = _codes(rows, cols, dev)
+    s = torch.empty((_cdiv(rows, 128), _cdiv(cols, 128)), dtype=torch.uint8, device=dev)
     st = fp8_quantize_block(w.data_ptr(), _in_dtype(w), rows, cols, _ld(w), fmt, q.data_ptr(), _ld(q),
-                            s.data_ptr(), _stream(stream))
+                            s.data_ptr(), _stream(stream, dev))
     _check(st, "fp8_quantize_block")
     return q, s
 
@@ -235,15 +329,16 @@ def quantize_block(w, fmt=E4M3, stream=None):
 def quantize_token_f32s(x, fmt=E4M3, axis=ROW, stream=None):
     """quantize_token with fp32 scales (float32 tensors in the same layouts)."""
     torch = _torch()
-    rows, cols = x.shape
+    rows, cols = _input(x, "x")
+    dev = _device_of([("x", x)])
     if axis == ROW:
-        q = _codes(rows, cols, x.device)
-        s = torch.empty((rows, (cols + 127) // 128), dtype=torch.float32, device=x.device)
+        q = _codes(rows, cols, dev)
+        s = torch.empty((rows, _cdiv(cols, 128)), dtype=torch.float32, device=dev)
     else:
-        q = _codes(cols, rows, x.device)
-        s = torch.empty((cols, (rows + 127) // 128), dtype=torch.float32, device=x.device)
+        q = _codes(cols, rows, dev)
+        s = torch.empty((cols, _cdiv(rows, 128)), dtype=torch.float32, device=dev)
     st = fp8_quantize_token_f32s(x.data_ptr(), _in_dtype(x), rows, cols, _ld(x), axis, fmt, q.data_ptr(), _ld(q),
-                                 s.data_ptr(), _stream(stream))
+                                 s.data_ptr(), _stream(stream, dev))
     _check(st, "fp8_quantize_token_f32s")
     return q, s
 
@@ -251,11 +346,12 @@ def quantize_token_f32s(x, fmt=E4M3, axis=ROW, stream=None):
 def quantize_block_f32s(w, fmt=E4M3, stream=None):
     """quantize_block with fp32 scales."""
     torch = _torch()
-    rows, cols = w.shape
-    q = _codes(rows, cols, w.device)
-    s = torch.empty(((rows + 127) // 128, (cols + 127) // 128), dtype=torch.float32, device=w.device)
+    rows, cols = _input(w, "w")
+    dev = _device_of([("w", w)])
+    q = _codes(rows, cols, dev)
+    s = torch.empty((_cdiv(rows, 128), _cdiv(cols, 128)), dtype=torch.float32, device=dev)
     st = fp8_quantize_block_f32s(w.data_ptr(), _in_dtype(w), rows, cols, _ld(w), fmt, q.data_ptr(), _ld(q),
-                                 s.data_ptr(), _stream(stream))
+                                 s.data_ptr(), _stream(stream, dev))
     _check(st, "fp8_quantize_block_f32s")
     return q, s
 
@@ -264,13 +360,14 @@ def quantize_token_dual(x, fmt=E4M3, stream=None):
     """Both token orientations from one read: (q, scales) as quantize_token ROW and
     (qt, scales_t) as quantize_token COL_T."""
     torch = _torch()
-    rows, cols = x.shape
-    q = _codes(rows, cols, x.device)
-    s = torch.empty((rows, (cols + 127) // 128), dtype=torch.uint8, device=x.device)
-    qt = _codes(cols, rows, x.device)
-    st = torch.empty((cols, (rows + 127) // 128), dtype=torch.uint8, device=x.device)
+    rows, cols = _input(x, "x")
+    dev = _device_of([("x", x)])
+    q = _codes(rows, cols, dev)
+    s = torch.empty((rows, _cdiv(cols, 128)), dtype=torch.uint8, device=dev)
+    qt = _codes(cols, rows, dev)
+    st = torch.empty((cols, _cdiv(rows, 128)), dtype=torch.uint8, device=dev)
     r = fp8_quantize_token_dual(x.data_ptr(), _in_dtype(x), rows, cols, _ld(x), fmt, q.data_ptr(), _ld(q),
-                                s.data_ptr(), qt.data_ptr(), _ld(qt), st.data_ptr(), _stream(stream))
+                                s.data_ptr(), qt.data_ptr(), _ld(qt), st.data_ptr(), _stream(stream, dev))
     _check(r, "fp8_quantize_token_dual")
     return q, s, qt, st
 
@@ -278,13 +375,14 @@ def quantize_token_dual(x, fmt=E4M3, stream=None):
 def quantize_block_dual(w, fmt=E4M3, stream=None):
     """128x128 block quantization with the transposed codes: (q, scales, qt, scales_t)."""
     torch = _torch()
-    rows, cols = w.shape
-    q = _codes(rows, cols, w.device)
-    s = torch.empty(((rows + 127) // 128, (cols + 127) // 128), dtype=torch.uint8, device=w.device)
-    qt = _codes(cols, rows, w.device)
-    st = torch.empty(((cols + 127) // 128, (rows + 127) // 128), dtype=torch.uint8, device=w.device)
+    rows, cols = _input(w, "w")
+    dev = _device_of([("w", w)])
+    q = _codes(rows, cols, dev)
+    s = torch.empty((_cdiv(rows, 128), _cdiv(cols, 128)), dtype=torch.uint8, device=dev)
+    qt = _codes(cols, rows, dev)
+    st = torch.empty((_cdiv(cols, 128), _cdiv(rows, 128)), dtype=torch.uint8, device=dev)
     r = fp8_quantize_block_dual(w.data_ptr(), _in_dtype(w), rows, cols, _ld(w), fmt, q.data_ptr(), _ld(q),
-                                s.data_ptr(), qt.data_ptr(), _ld(qt), st.data_ptr(), _stream(stream))
+                                s.data_ptr(), qt.data_ptr(), _ld(qt), st.data_ptr(), _stream(stream, dev))
     _check(r, "fp8_quantize_block_dual")
     return q, s, qt, st
 
@@ -292,76 +390,117 @@ def quantize_block_dual(w, fmt=E4M3, stream=None):
 def quantize_mx(x, fmt=E4M3, rule=RULE_FLOOR, counts=True, stream=None):
     """MX 32-element quantization: (q, scales [rows][cols/32], counts [rows][cols/32] or None)."""
     torch = _torch()
-    rows, cols = x.shape
-    q = _codes(rows, cols, x.device)
-    s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
-    c = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device) if counts else None
+    rows, cols = _input(x, "x")
+    _require(cols % 32 == 0, "x must have a multiple of 32 columns, got %d" % cols)
+    dev = _device_of([("x", x)])
+    q = _codes(rows, cols, dev)
+    s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+    c = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev) if counts else None
     st = mx_quantize(x.data_ptr(), _in_dtype(x), rows, cols, _ld(x), fmt, rule, q.data_ptr(), _ld(q),
-                     s.data_ptr(), c.data_ptr() if counts else None, _stream(stream))
+                     s.data_ptr(), c.data_ptr() if counts else None, _stream(stream, dev))
     _check(st, "mx_quantize")
     return q, s, c
 
 
-def block_scaled_gemm(a, a_scales, a_fmt, b, b_scales, b_fmt, b_layout=B_NK, b_scale_mode=SCALE_BLOCK128,
-                      out_dtype=None, out=None, stream=None):
-    """C = A * B over block-scaled FP8 codes (uint8 tensors), fp32 accumulation."""
-    torch = _torch()
+def _gemm_operands(a, a_scales, b, b_scales, b_layout, b_scale_mode, scale_dtypes, what):
+    """Checks the operands of the block-scaled GEMMs; returns (M, N, K)."""
+    _require(b_layout in (B_NK, B_KN), "b_layout must be B_NK or B_KN, got %r" % (b_layout,))
+    _require(b_scale_mode in (SCALE_BLOCK128, SCALE_ROW128),
+             "b_scale_mode must be SCALE_BLOCK128 or SCALE_ROW128, got %r" % (b_scale_mode,))
+    _require(not (b_layout == B_KN and b_scale_mode == SCALE_ROW128), "%s: per-row B scales need B stored [N][K]"
+             % what)
+    _require(_is_tensor(a) and a.dim() == 2, "a must be a 2-D torch tensor")
+    _require(_is_tensor(b) and b.dim() == 2, "b must be a 2-D torch tensor")
     M, K = a.shape
     N = b.shape[0] if b_layout == B_NK else b.shape[1]
-    if out is None:
-        dt = torch.float32 if out_dtype in (None, torch.float32) else torch.bfloat16
-        buf = torch.empty((M, _pad16(max(N, 1))), dtype=dt, device=a.device)
-        out = buf[:, :N]
-    c_dtype = F32 if out.dtype == torch.float32 else BF16
+    _require(K % 128 == 0, "%s: K must be a multiple of 128, got %d" % (what, K))
+    codes = _code_dtypes()
+    _matrix(a, "a", codes, (M, K))
+    _matrix(b, "b", codes, (N, K) if b_layout == B_NK else (K, N))
+    _dense(a_scales, "a_scales", scale_dtypes, (M, K // 128))
+    if b_scale_mode == SCALE_ROW128:
+        sb_shape = (N, K // 128)
+    elif b_layout == B_NK:
+        sb_shape = (_cdiv(N, 128), K // 128)
+    else:
+        sb_shape = (K // 128, _cdiv(N, 128))
+    _dense(b_scales, "b_scales", scale_dtypes, sb_shape)
+    return M, N, K
+
+
+def block_scaled_gemm(a, a_scales, a_fmt, b, b_scales, b_fmt, b_layout=B_NK, b_scale_mode=SCALE_BLOCK128,
+                      out_dtype=None, out=None, stream=None):
+    """C = A * B over block-scaled FP8 codes (uint8 or float8 tensors) with E8M0 scale
+    bytes (uint8 or float8_e8m0fnu), fp32 accumulation.  a [M][K] with a_scales
+    [M][K/128]; b [N][K] (B_NK) or [K][N] (B_KN) with b_scales [ceil(N/128)][K/128]
+    (B_NK, SCALE_BLOCK128), [K/128][ceil(N/128)] (B_KN) or [N][K/128] (SCALE_ROW128)."""
+    M, N, K = _gemm_operands(a, a_scales, b, b_scales, b_layout, b_scale_mode, _scale_dtypes(),
+                             "block_scaled_gemm")
+    _check_out(out, out_dtype, M, N)
+    dev = _device_of([("a", a), ("a_scales", a_scales), ("b", b), ("b_scales", b_scales)]
+                     + ([("out", out)] if out is not None else []))
+    out = _out_matrix(out, out_dtype, M, N, dev)
+    c_dtype = F32 if out.dtype == _torch().float32 else BF16
     st = fp8_block_scaled_gemm(M, N, K, a.data_ptr(), _ld(a), a_fmt, a_scales.data_ptr(), b.data_ptr(), _ld(b),
                                b_fmt, b_layout, b_scales.data_ptr(), b_scale_mode, out.data_ptr(), _ld(out),
-                               c_dtype, _stream(stream))
+                               c_dtype, _stream(stream, dev))
     _check(st, "fp8_block_scaled_gemm")
     return out
 
 
 def mx_scaled_gemm(a, a_scales, a_fmt, b, b_scales, b_fmt, out_dtype=None, out=None, stream=None):
-    """C = A * B^T over MX codes: a [M][K], b [N][K], scales [rows][K/32] (quantize_mx's layout)."""
-    torch = _torch()
+    """C = A * B^T over MX codes: a [M][K], b [N][K], scales [M][K/32] and [N][K/32]
+    (quantize_mx's layout; uint8 or float8_e8m0fnu)."""
+    _require(_is_tensor(a) and a.dim() == 2, "a must be a 2-D torch tensor")
+    _require(_is_tensor(b) and b.dim() == 2, "b must be a 2-D torch tensor")
     M, K = a.shape
     N = b.shape[0]
-    if out is None:
-        dt = torch.float32 if out_dtype in (None, torch.float32) else torch.bfloat16
-        buf = torch.empty((M, _pad16(max(N, 1))), dtype=dt, device=a.device)
-        out = buf[:, :N]
-    c_dtype = F32 if out.dtype == torch.float32 else BF16
+    _require(K % 128 == 0, "mx_scaled_gemm: K must be a multiple of 128, got %d" % K)
+    codes = _code_dtypes()
+    _matrix(a, "a", codes, (M, K))
+    _matrix(b, "b", codes, (N, K))
+    _dense(a_scales, "a_scales", _scale_dtypes(), (M, K // 32))
+    _dense(b_scales, "b_scales", _scale_dtypes(), (N, K // 32))
+    _check_out(out, out_dtype, M, N)
+    dev = _device_of([("a", a), ("a_scales", a_scales), ("b", b), ("b_scales", b_scales)]
+                     + ([("out", out)] if out is not None else []))
+    out = _out_matrix(out, out_dtype, M, N, dev)
+    c_dtype = F32 if out.dtype == _torch().float32 else BF16
     st = mx_gemm(M, N, K, a.data_ptr(), _ld(a), a_fmt, a_scales.data_ptr(), b.data_ptr(), _ld(b), b_fmt,
-                 b_scales.data_ptr(), out.data_ptr(), _ld(out), c_dtype, _stream(stream))
+                 b_scales.data_ptr(), out.data_ptr(), _ld(out), c_dtype, _stream(stream, dev))
     _check(st, "mx_gemm")
     return out
 
 
 def gemm_f32s(a, a_scales, a_fmt, b, b_scales, b_fmt, b_layout=B_NK, b_scale_mode=SCALE_BLOCK128,
               out_dtype=None, out=None, stream=None):
-    """block_scaled_gemm over operands with fp32 (float32 tensor) scales."""
-    torch = _torch()
-    M, K = a.shape
-    N = b.shape[0] if b_layout == B_NK else b.shape[1]
-    if out is None:
-        dt = torch.float32 if out_dtype in (None, torch.float32) else torch.bfloat16
-        buf = torch.empty((M, _pad16(max(N, 1))), dtype=dt, device=a.device)
-        out = buf[:, :N]
-    c_dtype = F32 if out.dtype == torch.float32 else BF16
+    """block_scaled_gemm over operands with fp32 scales (float32 tensors, same shapes)."""
+    M, N, K = _gemm_operands(a, a_scales, b, b_scales, b_layout, b_scale_mode, (_torch().float32,), "gemm_f32s")
+    _check_out(out, out_dtype, M, N)
+    dev = _device_of([("a", a), ("a_scales", a_scales), ("b", b), ("b_scales", b_scales)]
+                     + ([("out", out)] if out is not None else []))
+    out = _out_matrix(out, out_dtype, M, N, dev)
+    c_dtype = F32 if out.dtype == _torch().float32 else BF16
     st = fp8_gemm_f32s(M, N, K, a.data_ptr(), _ld(a), a_fmt, a_scales.data_ptr(), b.data_ptr(), _ld(b), b_fmt,
                        b_layout, b_scales.data_ptr(), b_scale_mode, out.data_ptr(), _ld(out), c_dtype,
-                       _stream(stream))
+                       _stream(stream, dev))
     _check(st, "fp8_gemm_f32s")
     return out
 
 
 def gaussws(w, bitwidths, seed, stream_id=0, out=None, stream=None):
-    """GaussWS sampled weight (bf16 tensor) of w with int8 bitwidths per 32x32 block."""
+    """GaussWS sampled weight (bf16 tensor) of w with int8 bitwidths per 32x32 block
+    ([ceil(rows/32)][ceil(cols/32)], contiguous)."""
     torch = _torch()
-    rows, cols = w.shape
+    rows, cols = _input(w, "w")
+    _dense(bitwidths, "bitwidths", (torch.int8,), (_cdiv(rows, 32), _cdiv(cols, 32)))
+    if out is not None:
+        _matrix(out, "out", (torch.bfloat16,), (rows, cols))
+    dev = _device_of([("w", w), ("bitwidths", bitwidths)] + ([("out", out)] if out is not None else []))
     if out is None:
-        buf = torch.empty((rows, _pad16(max(cols, 1))), dtype=torch.bfloat16, device=w.device)
+        buf = torch.empty((rows, _pad16(max(cols, 1))), dtype=torch.bfloat16, device=dev)
         out = buf[:, :cols]
     st = gaussws_sample(w.data_ptr(), _in_dtype(w), rows, cols, _ld(w), bitwidths.data_ptr(), seed, stream_id,
-                        out.data_ptr(), _ld(out), _stream(stream))
+                        out.data_ptr(), _ld(out), _stream(stream, dev))
     _check(st, "gaussws_sample")
     return out

@@ -1,5 +1,6 @@
 """Helpers for the GPU parity tests: host <-> device marshalling and the
 tolerances of the block-scaled GEMM."""
+import json
 import os
 
 import numpy as np
@@ -37,13 +38,27 @@ def host(t):
     return t.cpu().numpy()
 
 
-def gemm_tolerance(y_ref, t_ref, bf16_out):
-    """Per-element bound: 2^-12 * sum|a*b| for fp32 output; one extra bf16 rounding
-    (unit roundoff 2^-8 of a value within 2^-12 * t of y) for bf16 output."""
-    tol = 2.0 ** -12 * t_ref
+def gemm_tolerance(y_ref, t_ref, bf16_out, extra_rel=0.0):
+    """Per-element bound: 2^-12 * sum|a*b| (plus extra_rel * sum|a*b| where a variant
+    adds a documented term) for fp32 output; one extra bf16 rounding (unit roundoff
+    2^-8 of a value within that bound of y) for bf16 output."""
+    tol = (2.0 ** -12 + extra_rel) * t_ref
     if bf16_out:
-        tol = tol + 2.0 ** -8 * (np.abs(y_ref) + 2.0 ** -12 * t_ref)
+        tol = tol + 2.0 ** -8 * (np.abs(y_ref) + tol)
     return tol
+
+
+def record_ratio(what, ratio, n, over=0):
+    """Appends the largest err / bound of a comparison, its element count and the count
+    above the bound as a JSON line to the file named by MXFP8_RATIO_LOG, if set, tagged
+    with the running test."""
+    path = os.environ.get("MXFP8_RATIO_LOG")
+    if not path:
+        return
+    rec = {"test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0], "what": what,
+           "max_err_over_bound": float(ratio), "elements": int(n), "over_bound": int(over)}
+    with open(path, "a") as f:
+        f.write(json.dumps(rec) + "\n")
 
 
 def _exponent_field(codes, fmt):
@@ -60,14 +75,14 @@ def _exponent_field(codes, fmt):
 def mfma_alignment_bound(a, sa, a_fmt, b_nk, sb_nk, b_fmt, b_scale):
     """Per-element error bound of the FP8 matrix cores for adversarial operands.
 
-    Measured on gfx950: the scaled FP8 MFMA adds the products of each run of 8
-    consecutive k after aligning them to the run's largest exponent sum
-    E = max(e_a + e_b), keeping bits down to 2^(E-13) and truncating the rest
-    toward zero; the runs' sums then accumulate in fp32.  Each of the <= 8
-    products of a run therefore loses less than 2^(E-13), times the run's
-    scale.  For operands whose products span a narrow range this is far below
-    2^-12 * sum|a*b|; for uniformly random codes (products spanning ~50
-    binades) it can exceed it.  a: [M][K] codes, b_nk: [N][K] codes,
+    Measured on gfx950 (every FP8 MFMA form): the products of each run of 8
+    consecutive k are aligned to the run's largest exponent sum
+    E = max(e_a + e_b), bits below 2^(E-13) are truncated toward zero, and the
+    runs' sums accumulate in fp32.  Each of the <= 8 products of a run
+    therefore loses less than 2^(E-13), times the run's scale.  For operands
+    whose products span a narrow range this is far below 2^-12 * sum|a*b|; for
+    uniformly random codes (products spanning ~50 binades) an element can
+    exceed that by a few percent, rarely.  a: [M][K] codes, b_nk: [N][K] codes,
     sb_nk: per-row [N][K/128] (b_scale ROW128) or per-block [ceil(N/128)][K/128]."""
     M, K = a.shape
     N = b_nk.shape[0]
@@ -121,22 +136,42 @@ def mx_alignment_bound_at(a, sa, a_fmt, b_nk, sb, b_fmt, ii, jj):
     return (8.0 * np.exp2((E - 13 + sc).astype(np.float64))).sum(axis=1)
 
 
-def assert_gemm_close(y_gpu, y_ref, t_ref, bf16_out, what="", hw_bound=None):
-    """|y_gpu - y| <= 2^-12 * sum|a*b| (+ bf16 rounding).  With hw_bound (the
-    matrix cores' own alignment bound, for adversarial operands) the larger of
-    the two applies."""
+def assert_gemm_close(y_gpu, y_ref, t_ref, bf16_out, what="", extra_rel=0.0, hw_bound=None, max_over_plain=0):
+    """|y_gpu - y| <= 2^-12 * sum|a*b| (+ one bf16 rounding for bf16 output), element
+    by element; every output must be finite.
+
+    Adversarial random-code tests pass hw_bound, the matrix cores' own alignment
+    bound (mfma_alignment_bound): then at most max_over_plain elements may exceed the
+    plain bound, and those must stay within hw_bound.  The largest err / plain bound
+    and the count above it are recorded (record_ratio)."""
+    y_gpu = np.asarray(y_gpu)
     err = np.abs(y_gpu.astype(np.float64) - y_ref)
-    tol = gemm_tolerance(y_ref, t_ref, bf16_out)
-    if hw_bound is not None:
+    tol = gemm_tolerance(y_ref, t_ref, bf16_out, extra_rel)
+    assert np.isfinite(y_gpu).all(), what + ": non-finite output"
+    ratio = err / np.maximum(tol, np.finfo(np.float64).tiny)
+    ratio = np.where(err == 0, 0.0, ratio)
+    over = err > tol
+    record_ratio(what, ratio.max() if ratio.size else 0.0, ratio.size, int(over.sum()))
+    if hw_bound is None or not over.any():
+        bad = over
+    else:
+        assert int(over.sum()) <= max_over_plain, "%s: %d elements above the plain bound (cap %d); worst ratio %.4f" % (
+            what, int(over.sum()), max_over_plain, float(ratio.max()))
         hb = hw_bound + 2.0 ** -20 * t_ref
         if bf16_out:
             hb = hb + 2.0 ** -8 * (np.abs(y_ref) + hb)
         tol = np.maximum(tol, hb)
-    bad = err > tol
-    assert np.isfinite(y_gpu).all(), what + ": non-finite output"
+        bad = err > tol
     assert not bad.any(), "%s: %d elements out of tolerance; worst err %.3e tol %.3e at %s" % (
         what, int(bad.sum()), float(err[bad].max()), float(tol[bad][np.argmax(err[bad])]),
         str(np.argwhere(bad)[0]))
+
+
+def adversarial_cap(n):
+    """Elements of an n-element random-code product allowed above the plain bound: one
+    per 100,000 (at least one).  The matrix-core model puts the rate near one per
+    400,000 for uniformly random codes."""
+    return max(1, n // 100000)
 
 
 def run_gemm(a, sa, a_fmt, b, sb, b_fmt, b_layout, b_scale, bf16_out):

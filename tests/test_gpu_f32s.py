@@ -1,8 +1,9 @@
 """GPU parity of the fp32-scale variant ("FP8 w. FP32 scale"): the quantizers
 must match the oracle byte for byte (codes) and bit for bit (fp32 scales); the
 GEMM must stay within 2^-12 * sum|a*b| (+ 2^-22 * sum|a*b| for the rounding of
-the fp32 scale product, + one bf16 rounding), widened to the matrix cores' own
-alignment bound for arbitrary codes.  Calls go through the C ABI."""
+the fp32 scale product, + one bf16 rounding; on uniformly random codes a
+capped count of elements may exceed it within the matrix cores' alignment
+bound).  Calls go through the C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +11,7 @@ import torch
 import mx_block_scaled_x128_amd as mx
 import oracle
 import synth
-from gpu_helpers import ORACLE_THREADS, _exponent_field, dev, dev_ld16, host
+from gpu_helpers import ORACLE_THREADS, _exponent_field, adversarial_cap, assert_gemm_close, dev, dev_ld16, host
 from test_gpu_quant import edge_case_rows
 
 pytestmark = pytest.mark.gpu
@@ -100,17 +101,11 @@ def alignment_bound(a, sa, a_fmt, b_nk, sb_cols, b_fmt):
 
 
 def assert_close(y, y_ref, t_ref, bf16_out, what, hw=None):
-    tol = 2.0 ** -12 * t_ref
-    if hw is not None:
-        tol = np.maximum(tol, hw + 2.0 ** -20 * t_ref)
-    tol = tol + 2.0 ** -22 * t_ref
-    if bf16_out:
-        tol = tol + 2.0 ** -8 * (np.abs(y_ref) + tol)
-    err = np.abs(y.astype(np.float64) - y_ref)
-    assert np.isfinite(y).all(), what
-    bad = err > tol
-    assert not bad.any(), "%s: %d bad, worst err %.3e tol %.3e at %s" % (
-        what, int(bad.sum()), float(err[bad].max()), float(tol[bad][np.argmax(err[bad])]), np.argwhere(bad)[0])
+    """The block GEMM's bound plus 2^-22 * sum|a*b| for the rounding of the fp32 scale
+    product fl(sa * sb) that each K block's partial sum is multiplied by; with hw (the
+    alignment bound, random codes only) a capped count of elements may exceed it."""
+    assert_gemm_close(y, y_ref, t_ref, bf16_out, what, extra_rel=2.0 ** -22, hw_bound=hw,
+                      max_over_plain=adversarial_cap(np.size(y)) if hw is not None else 0)
 
 
 def run(a, sa, a_fmt, b, sb, b_fmt, b_layout, b_scale, bf16_out):
@@ -192,7 +187,7 @@ def test_gemm_k_zero_and_ldc():
 @pytest.mark.parametrize("bf16_out", [False, True])
 def test_quantize_then_gemm_plain_bound(bf16_out):
     """fp32-scale quantizers on the GPU (bit-exact with the oracle), then the
-    GEMM on those operands, held to the plain bound (no alignment widening)."""
+    GEMM on those operands."""
     M, N, K = 300, 520, 1024
     x = synth.activations_like(91, (M, K), bf16=True)
     w = synth.weights_like(92, (N, K), bf16=True)
@@ -211,8 +206,7 @@ def test_quantize_then_gemm_plain_bound(bf16_out):
 
 def test_fprop_1p5b_full_size():
     """The fprop shape (X 4096x1536, W 8960x1536 bf16) with fp32 scales: the
-    quantizers compared in full, the GEMM on sampled elements at the plain bound."""
-    from test_gpu_workloads import sample_points
+    quantizers and the GEMM compared in full."""
     d = synth.fprop1p5b()
     xq, xs = mx.quantize_token_f32s(dev(d["x"]), mx.E4M3, mx.ROW)
     wq, ws = mx.quantize_block_f32s(dev(d["w"]), mx.E4M3)
@@ -222,7 +216,5 @@ def test_fprop_1p5b_full_size():
     wq_ref, ws_ref = oracle.quantize_block_f32s(d["w"], oracle.E4M3, threads=ORACLE_THREADS)
     assert np.array_equal(host(xs), xs_ref) and np.array_equal(host(xq), xq_ref)
     assert np.array_equal(host(ws), ws_ref) and np.array_equal(host(wq), wq_ref)
-    yh = host(y)
-    ii, jj = sample_points(*yh.shape, 77)
-    y_ref, t_ref = oracle.gemm_f32s_elems(xq_ref, xs_ref, 0, wq_ref, ws_ref, 0, ii, jj, threads=ORACLE_THREADS)
-    assert_close(yh[ii, jj], y_ref, t_ref, True, "f32s fprop")
+    y_ref, t_ref = oracle.gemm_f32s(xq_ref, xs_ref, 0, wq_ref, ws_ref, 0, threads=ORACLE_THREADS)
+    assert_close(host(y), y_ref, t_ref, True, "f32s fprop1p5b")

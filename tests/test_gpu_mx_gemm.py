@@ -1,8 +1,8 @@
 """GPU parity of the MX GEMM (FP8 operands with one E8M0 scale per 32
 elements along K) against the CPU oracle (fp64 over dequantized operands),
 through the C ABI.  Bound per element: |y_gpu - y| <= 2^-12 * sum_k |a*b|
-(+ one bf16 rounding), widened to the matrix cores' alignment bound for
-arbitrary codes."""
+(+ one bf16 rounding for bf16 output); on uniformly random codes a capped
+count of elements may exceed it within the matrix cores' alignment bound."""
 import numpy as np
 import pytest
 import torch
@@ -10,8 +10,8 @@ import torch
 import mx_block_scaled_x128_amd as mx
 import oracle
 import synth
-from gpu_helpers import (ORACLE_THREADS, assert_gemm_close, dev, dev_ld16, host, mx_alignment_bound,
-                         mx_alignment_bound_at, run_mx_gemm)
+from gpu_helpers import (ORACLE_THREADS, adversarial_cap, assert_gemm_close, dev, dev_ld16, host,
+                         mx_alignment_bound, mx_alignment_bound_at, run_mx_gemm)
 
 pytestmark = pytest.mark.gpu
 
@@ -79,7 +79,8 @@ def test_random_codes_parity(a_fmt, b_fmt, bf16_out, shape):
     y = run_mx_gemm(a, sa, a_fmt, b, sb, b_fmt, bf16_out)
     y_ref, t_ref = oracle.mx_gemm(a, sa, a_fmt, b, sb, b_fmt, threads=8)
     hb = mx_alignment_bound(a, sa, a_fmt, b, sb, b_fmt)
-    assert_gemm_close(y, y_ref, t_ref, bf16_out, "mx random codes %s" % (shape,), hw_bound=hb)
+    assert_gemm_close(y, y_ref, t_ref, bf16_out, "mx random codes %s" % (shape,), hw_bound=hb,
+                      max_over_plain=adversarial_cap(y.size))
 
 
 def test_k_zero_writes_zeros():
@@ -105,7 +106,8 @@ def test_ldc_larger_than_n_leaves_padding():
     torch.cuda.synchronize()
     ch = host(c)
     y_ref, t_ref = oracle.mx_gemm(a, sa, 0, b, sb, 0)
-    assert_gemm_close(ch[:, :N], y_ref, t_ref, False, "ldc", hw_bound=mx_alignment_bound(a, sa, 0, b, sb, 0))
+    assert_gemm_close(ch[:, :N], y_ref, t_ref, False, "ldc", hw_bound=mx_alignment_bound(a, sa, 0, b, sb, 0),
+                      max_over_plain=adversarial_cap(M * N))
     assert np.all(ch[:, N:] == -1.0)
 
 
@@ -146,13 +148,14 @@ def test_short_last_round_as_quadrants(bf16_out):
     r0 = 256 * 16
     y_ref, t_ref = oracle.mx_gemm(a[r0:], sa[r0:], 0, b, sb, 1, threads=8)
     hb = mx_alignment_bound(a[r0:], sa[r0:], 0, b, sb, 1)
-    assert_gemm_close(y[r0:], y_ref, t_ref, bf16_out, "quadrant rows", hw_bound=hb)
+    assert_gemm_close(y[r0:], y_ref, t_ref, bf16_out, "quadrant rows", hw_bound=hb,
+                      max_over_plain=adversarial_cap(y_ref.size))
     rng = np.random.default_rng(seed)
     ii = np.concatenate([rng.integers(r0 - 256, r0, 2048), rng.integers(0, r0, 512)])
     jj = rng.integers(0, N, ii.size)
     y_s, t_s = oracle.mx_gemm_elems(a, sa, 0, b, sb, 1, ii, jj, threads=8)
     hb_s = mx_alignment_bound_at(a, sa, 0, b, sb, 1, ii, jj)
-    assert_gemm_close(y[ii, jj], y_s, t_s, bf16_out, "sampled", hw_bound=hb_s)
+    assert_gemm_close(y[ii, jj], y_s, t_s, bf16_out, "sampled", hw_bound=hb_s, max_over_plain=adversarial_cap(ii.size))
 
 
 def test_strided_operands():
@@ -165,4 +168,5 @@ def test_strided_operands():
     y = mx.mx_scaled_gemm(dev(a, pitch=K + 48), dev(sa), 1, dev(b, pitch=K + 16), dev(sb), 0)
     torch.cuda.synchronize()
     y_ref, t_ref = oracle.mx_gemm(a, sa, 1, b, sb, 0, threads=8)
-    assert_gemm_close(host(y), y_ref, t_ref, False, "strided", hw_bound=mx_alignment_bound(a, sa, 1, b, sb, 0))
+    assert_gemm_close(host(y), y_ref, t_ref, False, "strided", hw_bound=mx_alignment_bound(a, sa, 1, b, sb, 0),
+                      max_over_plain=adversarial_cap(M * N))
