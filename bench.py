@@ -8,12 +8,12 @@ resident in HBM:
   3. fp8_block_scaled_gemm  dX = dYq * Wq, M=8192 N=3584 K=18944 (W stored [K][N]),
      fp32 accumulation, bf16 out
 `value` is the whole step's throughput in TFLOP/s (2*M*N*K per step / step time),
-with consecutive steps captured in a HIP graph and replayed (the launches are
-asynchronous and allocate nothing, so a replay is the same work without the host's
-per-launch cost).  In a separate eager pass each entry point is timed with events
-on the stream it runs on, and the dominant one (the GEMM) is reported against the
-dense FP8 MFMA peak (`roofline`).  `cpu_baseline` times the CPU oracle on a
-bounded sample of the same step.
+with the steps' asynchronous calls enqueued back to back between two device
+synchronisations.  In a second pass each entry point is timed with events on the
+stream it runs on, and the dominant one (the GEMM) is reported against the dense
+FP8 MFMA peak (`roofline`).  The same steps replayed from a captured HIP graph are
+reported as context (the calls allocate and synchronise nothing, so they capture).
+`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 
 Other workloads (--workload) print the same kind of line: fprop1p5b (forward of
 a 1.5B-class layer), wgrad (weight gradient from column-quantized activations and
@@ -231,9 +231,42 @@ def time_graph(step, steps, warmup, outputs):
     return (time.perf_counter() - t0) / steps, per_graph
 
 
+def ramp(step, min_seconds=0.3, min_steps=1):
+    """Untimed steps until the device has been busy for min_seconds (and at least
+    min_steps): the GPU raises its clock over the first tens of milliseconds of
+    sustained load (measured on the dgrad step: the first ~40 steps run the GEMM 5-85 %
+    slower than the steady ~410 us), which a few warmup steps after an idle host phase
+    do not cover.  Returns the number of steps run."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while n < min_steps or time.perf_counter() - t0 < min_seconds:
+        for _ in range(4):
+            step(_NoTimer())
+        n += 4
+        torch.cuda.synchronize()
+    return n
+
+
+def time_plain(step, steps, warmup):
+    """`warmup` untimed steps, then `steps` steps launched back to back from Python
+    between two device synchronisations, with nothing else on the stream: the host
+    enqueues the asynchronous calls far faster than the device runs them, so the wall
+    time is the device's time for the step.  Returns seconds per step."""
+    import torch
+    for _ in range(warmup):
+        step(_NoTimer())
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(_NoTimer())
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
 def time_steps(step, steps, warmup):
-    """The eager pass: `steps` steps launched from Python, each entry point between an
-    event pair.  Returns (seconds per step, timer)."""
+    """The eager pass with events: `steps` steps launched from Python, each entry point
+    between an event pair.  Returns (seconds per step, timer)."""
     import torch
     timer = KernelTimer()
     for _ in range(warmup):
@@ -706,8 +739,10 @@ def bench_workload(args):
     wl = SETUP[args.workload]()
     step, sizes, flops = wl["step"], wl["sizes"], wl["flops"]
     calls = wl.get("calls", {})
-    per_step_eager, timer = time_steps(step, args.steps, args.warmup)
-    per_step, per_graph = time_graph(step, args.steps, args.warmup, wl["outputs"])
+    ramp_steps = ramp(step, min_steps=args.warmup)
+    per_step = time_plain(step, args.steps, args.warmup)
+    per_step_events, timer = time_steps(step, args.steps, args.warmup)
+    per_step_graph, per_graph = time_graph(step, args.steps, args.warmup, wl["outputs"])
     kern = {}
     for name, b in sizes.items():
         t = timer.mean(name)
@@ -740,7 +775,9 @@ def bench_workload(args):
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(per_step * 1e3, 4),
-        "ms_per_step_eager": round(per_step_eager * 1e3, 4), "steps_per_graph": per_graph,
+        "ms_per_step_with_events": round(per_step_events * 1e3, 4),
+        "ms_per_step_graph": round(per_step_graph * 1e3, 4), "steps_per_graph": per_graph,
+        "clock_ramp_steps": ramp_steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl["dtype"],
         "data": "synthetic (seeded numpy PCG64; inputs resident in HBM before timing)",
         "config": config, "kernels": kern, "roofline": roof,
@@ -751,12 +788,17 @@ def bench_workload(args):
             if name in line["kernels"]:
                 line["kernels"][name].update(d)
         line["device"] = device
-    line["timing"] = ("value: replays of a graph of steps_per_graph whole steps between synchronisations; "
-                      "kernels.us: mean of event-bracketed eager calls inside the step, on the stream they run on "
+    line["timing"] = ("before any timing, clock_ramp_steps untimed steps (at least 0.3 s of sustained load, at "
+                      "least `warmup`) bring the GPU clock to its loaded steady state; then `warmup` untimed "
+                      "steps before each timed pass. "
+                      "value: `steps` whole steps launched back to back between two device synchronisations "
+                      "(ms_per_step); kernels.us: mean of event-bracketed calls in a second pass of `steps` steps "
+                      "(ms_per_step_with_events), on the stream they run on "
                       "(us_median: median); us_cold_median: each call after a 512 MiB scrub write, medians of 10; "
                       "roofline.achieved: from kernels.<kernel>.us; gemm.us_back_to_back: mean of GEMM calls "
                       "issued back to back between one event pair (operands left in the caches by the previous "
-                      "call: context, not the step)")
+                      "call: context, not the step); ms_per_step_graph: replays of a HIP graph of steps_per_graph "
+                      "steps (context: the captured step reproduces the eager outputs bit for bit)")
     cpu_stats = None
     if args.no_cpu:
         line["cpu_baseline"] = None

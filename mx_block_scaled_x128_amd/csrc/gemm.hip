@@ -641,10 +641,10 @@ __device__ __forceinline__ void gemm_tile(
   // instruction then covers whole 256-byte row segments.  The stores are
   // non-temporal: output lines are written once, and kept out of L2 they
   // leave the operand tiles other workgroups still read in place (measured:
-  // 5 % on the fprop shape, none lost elsewhere).  The staging sits
-  // in two ring slots nothing reads any more (waves 0, 1 in the first, 2, 3
-  // in the second); only the wave itself touches its region, and LDS
-  // executes one wave's accesses in order, so no barrier is needed.
+  // 5 % on the fprop shape, none lost elsewhere).  The staging sits in one
+  // K-block buffer nothing reads any more, each wave in its own 32-row region
+  // (stage_buf + wave * 32 * P); only the wave itself touches its region, and
+  // LDS executes one wave's accesses in order, so no barrier is needed.
   auto epilogue = [&](uint8_t* stage_buf) __attribute__((always_inline)) {
     if (!out_bf16) {
       constexpr int P = WN * 4 + 16;  // bytes per staged row

@@ -74,8 +74,10 @@ constexpr int kColPitch = 136;
 
 // A 128 x 128-byte tile of codes in LDS in the layout of the output (rows of
 // 128 bytes, no padding): the 8-byte chunk c of row r sits in 16-byte slot
-// (c >> 1) ^ ((r >> 3) & 7), half c & 1.  Writers (lane = row chunk r >> 3,
-// 8 rows apart, times chunk) hit 16 distinct slots per 16 lanes; readers take
+// (c >> 1) ^ ((r >> 3) & 7), half c & 1.  The writers (quant_dual_kernel: a
+// lane's 4 rows are 4 apart, 16 lanes cover 8 row groups and 2 chunks;
+// quant_block_dual_kernel: 8 rows 8 apart) put one chunk of many rows at once,
+// and the XOR spreads those rows' chunks over different slots; readers take
 // whole 16-byte slots.  Every store instruction then writes 8 full 128-byte
 // rows instead of 64-byte halves of lines from two different waves.
 __device__ __forceinline__ uint32_t row_tile_offset(uint32_t r, uint32_t c) {

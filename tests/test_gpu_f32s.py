@@ -104,7 +104,8 @@ def assert_close(y, y_ref, t_ref, bf16_out, what, hw=None):
     """The block GEMM's bound plus 2^-22 * sum|a*b| for the rounding of the fp32 scale
     product fl(sa * sb) that each K block's partial sum is multiplied by; with hw (the
     alignment bound, random codes only) a capped count of elements may exceed it."""
-    assert_gemm_close(y, y_ref, t_ref, bf16_out, what, extra_rel=2.0 ** -22, hw_bound=hw,
+    hw_fn = None if hw is None else (lambda idx: hw[idx])
+    assert_gemm_close(y, y_ref, t_ref, bf16_out, what, extra_rel=2.0 ** -22, hw_bound=hw_fn,
                       max_over_plain=adversarial_cap(np.size(y)) if hw is not None else 0)
 
 

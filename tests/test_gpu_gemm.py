@@ -8,8 +8,8 @@ import torch
 import mx_block_scaled_x128_amd as mx
 import oracle
 import synth
-from gpu_helpers import (adversarial_cap, assert_gemm_close, dev, host, mfma_alignment_bound,
-                         mfma_alignment_bound_at, run_gemm)
+from gpu_helpers import (adversarial_cap, alignment_bound_fn, assert_gemm_close, dev, host,
+                         run_gemm)
 
 pytestmark = pytest.mark.gpu
 
@@ -85,7 +85,7 @@ def test_each_scale_byte_moves_only_its_block(b_layout, b_scale):
     sb_store = sb if b_layout == mx.B_NK else np.ascontiguousarray(sb.T)
     y = run_gemm(a, sa, 0, b, sb_store, 0, b_layout, b_scale, False)
     y_ref, t_ref = oracle.gemm(a, sa, 0, b, sb_store, 0, b_layout, b_scale)
-    hb = mfma_alignment_bound(a, sa, 0, b_nk, sb, 0, b_scale)
+    hb = alignment_bound_fn(a, sa, 0, b_nk, sb, 0, b_scale)
     assert_gemm_close(y, y_ref, t_ref, False, "scale bump", hw_bound=hb, max_over_plain=adversarial_cap(y.size))
 
 
@@ -111,7 +111,7 @@ def test_random_codes_parity(a_fmt, b_fmt, b_layout, b_scale, bf16_out, shape):
     sb_store = sb if (b_layout == mx.B_NK) else np.ascontiguousarray(sb.T)
     y = run_gemm(a, sa, a_fmt, b, sb_store, b_fmt, b_layout, b_scale, bf16_out)
     y_ref, t_ref = oracle.gemm(a, sa, a_fmt, b, sb_store, b_fmt, b_layout, b_scale, threads=8)
-    hb = mfma_alignment_bound(a, sa, a_fmt, b_nk, sb, b_fmt, b_scale)
+    hb = alignment_bound_fn(a, sa, a_fmt, b_nk, sb, b_fmt, b_scale)
     assert_gemm_close(y, y_ref, t_ref, bf16_out, "random codes %s" % (shape,), hw_bound=hb,
                       max_over_plain=adversarial_cap(y.size))
 
@@ -167,7 +167,7 @@ def test_ldc_larger_than_n_leaves_padding():
     torch.cuda.synchronize()
     ch = host(c)
     y_ref, t_ref = oracle.gemm(a, sa, 0, b, sb, 0)
-    hb = mfma_alignment_bound(a, sa, 0, b, sb, 0, mx.SCALE_BLOCK128)
+    hb = alignment_bound_fn(a, sa, 0, b, sb, 0, mx.SCALE_BLOCK128)
     assert_gemm_close(ch[:, :N], y_ref, t_ref, False, "ldc", hw_bound=hb, max_over_plain=adversarial_cap(M * N))
     assert np.all(ch[:, N:] == -1.0)
 
@@ -211,14 +211,14 @@ def test_short_last_round_as_quadrants(b_layout, b_scale, bf16_out):
     assert np.isfinite(y).all()
     r0 = 256 * 16  # the quadrant row
     y_ref, t_ref = oracle.gemm(a[r0:], sa[r0:], 0, b, sb_store, 1, b_layout, b_scale, threads=8)
-    hb = mfma_alignment_bound(a[r0:], sa[r0:], 0, b_nk, sb, 1, b_scale)
+    hb = alignment_bound_fn(a[r0:], sa[r0:], 0, b_nk, sb, 1, b_scale)
     assert_gemm_close(y[r0:], y_ref, t_ref, bf16_out, "quadrant rows", hw_bound=hb,
                       max_over_plain=adversarial_cap(y_ref.size))
     rng = np.random.default_rng(seed)
     ii = np.concatenate([rng.integers(r0 - 256, r0, 2048), rng.integers(0, r0, 512)])
     jj = rng.integers(0, N, ii.size)
     y_s, t_s = oracle.gemm_elems(a, sa, 0, b, sb_store, 1, ii, jj, b_layout, b_scale, threads=8)
-    hb_s = mfma_alignment_bound_at(a, sa, 0, b_nk, sb, 1, b_scale, ii, jj)
+    hb_s = alignment_bound_fn(a, sa, 0, b_nk, sb, 1, b_scale, ii=ii, jj=jj)
     assert_gemm_close(y[ii, jj], y_s, t_s, bf16_out, "sampled", hw_bound=hb_s, max_over_plain=adversarial_cap(ii.size))
 
 

@@ -11,7 +11,7 @@ import mx_block_scaled_x128_amd as mx
 import oracle
 import synth
 from gpu_helpers import (ORACLE_THREADS, adversarial_cap, assert_gemm_close, dev, dev_ld16, host,
-                         mx_alignment_bound, mx_alignment_bound_at, run_mx_gemm)
+                         alignment_bound_fn, run_mx_gemm)
 
 pytestmark = pytest.mark.gpu
 
@@ -78,7 +78,7 @@ def test_random_codes_parity(a_fmt, b_fmt, bf16_out, shape):
     sb = synth.random_scale_bytes(seed + 3, (N, K // 32))
     y = run_mx_gemm(a, sa, a_fmt, b, sb, b_fmt, bf16_out)
     y_ref, t_ref = oracle.mx_gemm(a, sa, a_fmt, b, sb, b_fmt, threads=8)
-    hb = mx_alignment_bound(a, sa, a_fmt, b, sb, b_fmt)
+    hb = alignment_bound_fn(a, sa, a_fmt, b, sb, b_fmt, mx_scales=True)
     assert_gemm_close(y, y_ref, t_ref, bf16_out, "mx random codes %s" % (shape,), hw_bound=hb,
                       max_over_plain=adversarial_cap(y.size))
 
@@ -106,7 +106,7 @@ def test_ldc_larger_than_n_leaves_padding():
     torch.cuda.synchronize()
     ch = host(c)
     y_ref, t_ref = oracle.mx_gemm(a, sa, 0, b, sb, 0)
-    assert_gemm_close(ch[:, :N], y_ref, t_ref, False, "ldc", hw_bound=mx_alignment_bound(a, sa, 0, b, sb, 0),
+    assert_gemm_close(ch[:, :N], y_ref, t_ref, False, "ldc", hw_bound=alignment_bound_fn(a, sa, 0, b, sb, 0, mx_scales=True),
                       max_over_plain=adversarial_cap(M * N))
     assert np.all(ch[:, N:] == -1.0)
 
@@ -147,14 +147,14 @@ def test_short_last_round_as_quadrants(bf16_out):
     assert np.isfinite(y).all()
     r0 = 256 * 16
     y_ref, t_ref = oracle.mx_gemm(a[r0:], sa[r0:], 0, b, sb, 1, threads=8)
-    hb = mx_alignment_bound(a[r0:], sa[r0:], 0, b, sb, 1)
+    hb = alignment_bound_fn(a[r0:], sa[r0:], 0, b, sb, 1, mx_scales=True)
     assert_gemm_close(y[r0:], y_ref, t_ref, bf16_out, "quadrant rows", hw_bound=hb,
                       max_over_plain=adversarial_cap(y_ref.size))
     rng = np.random.default_rng(seed)
     ii = np.concatenate([rng.integers(r0 - 256, r0, 2048), rng.integers(0, r0, 512)])
     jj = rng.integers(0, N, ii.size)
     y_s, t_s = oracle.mx_gemm_elems(a, sa, 0, b, sb, 1, ii, jj, threads=8)
-    hb_s = mx_alignment_bound_at(a, sa, 0, b, sb, 1, ii, jj)
+    hb_s = alignment_bound_fn(a, sa, 0, b, sb, 1, mx_scales=True, ii=ii, jj=jj)
     assert_gemm_close(y[ii, jj], y_s, t_s, bf16_out, "sampled", hw_bound=hb_s, max_over_plain=adversarial_cap(ii.size))
 
 
@@ -168,5 +168,5 @@ def test_strided_operands():
     y = mx.mx_scaled_gemm(dev(a, pitch=K + 48), dev(sa), 1, dev(b, pitch=K + 16), dev(sb), 0)
     torch.cuda.synchronize()
     y_ref, t_ref = oracle.mx_gemm(a, sa, 1, b, sb, 0, threads=8)
-    assert_gemm_close(host(y), y_ref, t_ref, False, "strided", hw_bound=mx_alignment_bound(a, sa, 1, b, sb, 0),
+    assert_gemm_close(host(y), y_ref, t_ref, False, "strided", hw_bound=alignment_bound_fn(a, sa, 1, b, sb, 0, mx_scales=True),
                       max_over_plain=adversarial_cap(M * N))
