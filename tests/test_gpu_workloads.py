@@ -16,11 +16,15 @@ from gpu_helpers import ORACLE_THREADS, assert_gemm_close, dev, host
 pytestmark = pytest.mark.gpu
 
 
-def check_full_gemm(y_dev, a, sa, a_fmt, b, sb, b_fmt, b_layout, b_scale, bf16_out, what):
-    """Every output element against the oracle's fp64 product over the same codes."""
+def check_full_gemm(y_dev, a, sa, a_fmt, b, sb, b_fmt, b_layout, b_scale, bf16_out, what, y32_dev=None):
+    """Every output element against the oracle's fp64 product over the same codes; with
+    y32_dev (the same GEMM with fp32 output) also every element at the pure
+    2^-12 * sum|a*b| bound, without the bf16 rounding term."""
     y = host(y_dev)
     y_ref, t_ref = oracle.gemm(a, sa, a_fmt, b, sb, b_fmt, b_layout, b_scale, threads=ORACLE_THREADS)
     assert_gemm_close(y, y_ref, t_ref, bf16_out, what)
+    if y32_dev is not None:
+        assert_gemm_close(host(y32_dev), y_ref, t_ref, False, what.replace("bf16", "fp32"))
 
 
 def test_tiny_reference_full():
@@ -48,7 +52,9 @@ def test_fprop_1p5b():
     wq_ref, ws_ref = oracle.quantize_block(d["w"], oracle.E4M3, threads=ORACLE_THREADS)
     assert np.array_equal(host(xs), xs_ref) and np.array_equal(host(xq), xq_ref)
     assert np.array_equal(host(ws), ws_ref) and np.array_equal(host(wq), wq_ref)
-    check_full_gemm(y, xq_ref, xs_ref, 0, wq_ref, ws_ref, 0, 0, 0, True, "fprop1p5b bf16")
+    y32 = mx.block_scaled_gemm(xq, xs, mx.E4M3, wq, ws, mx.E4M3, mx.B_NK, mx.SCALE_BLOCK128)
+    torch.cuda.synchronize()
+    check_full_gemm(y, xq_ref, xs_ref, 0, wq_ref, ws_ref, 0, 0, 0, True, "fprop1p5b bf16", y32)
 
 
 def test_dgrad_7b():
@@ -63,7 +69,9 @@ def test_dgrad_7b():
     assert np.array_equal(host(gs), gs_ref) and np.array_equal(host(gq), gq_ref)
     wq_ref, ws_ref = oracle.quantize_block(d["w"], oracle.E4M3, threads=ORACLE_THREADS)
     assert np.array_equal(host(ws), ws_ref) and np.array_equal(host(wq), wq_ref)
-    check_full_gemm(y, gq_ref, gs_ref, 1, wq_ref, ws_ref, 0, 1, 0, True, "dgrad7b bf16")
+    y32 = mx.block_scaled_gemm(gq, gs, mx.E5M2, wq, ws, mx.E4M3, mx.B_KN, mx.SCALE_BLOCK128)
+    torch.cuda.synchronize()
+    check_full_gemm(y, gq_ref, gs_ref, 1, wq_ref, ws_ref, 0, 1, 0, True, "dgrad7b bf16", y32)
 
 
 @pytest.mark.parametrize("group", range(4))
@@ -99,8 +107,11 @@ def test_mx_fprop_1p5b():
     wq_ref, ws_ref, _ = oracle.mx_quantize(d["w"], oracle.E4M3, oracle.RULE_FLOOR, threads=ORACLE_THREADS)
     assert np.array_equal(host(xs), xs_ref) and np.array_equal(host(xq), xq_ref)
     assert np.array_equal(host(ws), ws_ref) and np.array_equal(host(wq), wq_ref)
+    y32 = mx.mx_scaled_gemm(xq, xs, mx.E4M3, wq, ws, mx.E4M3)
+    torch.cuda.synchronize()
     y_ref, t_ref = oracle.mx_gemm(xq_ref, xs_ref, 0, wq_ref, ws_ref, 0, threads=ORACLE_THREADS)
     assert_gemm_close(host(y), y_ref, t_ref, True, "mx fprop1p5b bf16")
+    assert_gemm_close(host(y32), y_ref, t_ref, False, "mx fprop1p5b fp32")
 
 
 def test_wgrad():
