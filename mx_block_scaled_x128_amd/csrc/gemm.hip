@@ -136,6 +136,12 @@ __device__ __forceinline__ void mfma_retire_pad() {
 #ifndef MXFP8_GEMM_DS_SPAN
 #define MXFP8_GEMM_DS_SPAN 3
 #endif
+// Fraction (in quarters) of the second stage's MFMAs over which the loads of
+// the K block two ahead are spread (earlier loads have longer to land before
+// the next K block's wait).
+#ifndef MXFP8_GEMM_DMA_SPAN
+#define MXFP8_GEMM_DMA_SPAN 4
+#endif
 
 // LDS of one tile body (bytes): two K-block buffers of PB bytes each, and the
 // scale-group areas (SGRP bytes).  See gemm_tile for the layouts.
@@ -321,12 +327,18 @@ __device__ __forceinline__ void gemm_tile(
     src.b = uniform_opaque(b_base + (int64_t)kb * b_step);
     return src;
   };
+  // The lane offsets are redefined (opaquely, in place) at each use: kept
+  // loop-invariant, they were widened to 64 bits outside the K loop (two
+  // VGPRs each, plus a 64-bit add per load) instead of feeding the
+  // scalar-base + 32-bit-offset form of the load.
   auto dma_item = [&](int p, const Src& src, int item) __attribute__((always_inline)) {
     uint8_t* buf = buf_ptr(p);
     if (item < A_LOADS) {
+      a_off[item] = opaque(a_off[item]);
       __builtin_amdgcn_global_load_lds(src.a + a_off[item], buf + (item * 4 + wave) * 1024, 16, 0, 0);
     } else {
       const int j = item - A_LOADS;
+      b_off[j] = opaque(b_off[j]);
       __builtin_amdgcn_global_load_lds(src.b + b_off[j], buf + A_ST + (j * 4 + wave) * 1024, 16, 0, 0);
     }
   };
@@ -488,6 +500,7 @@ __device__ __forceinline__ void gemm_tile(
   // MFMA pipe.  sched_barrier(0) keeps the order.
   constexpr int MFMAS = MT * NT;
   constexpr int DS_SPAN = MFMAS * MXFP8_GEMM_DS_SPAN / 4 > 0 ? MFMAS * MXFP8_GEMM_DS_SPAN / 4 : 1;
+  constexpr int DMA_SPAN = MFMAS * MXFP8_GEMM_DMA_SPAN / 4 > 0 ? MFMAS * MXFP8_GEMM_DMA_SPAN / 4 : 1;
   // The stage multiplies fragments (ca, cb) with scales (csa, csb).
   // dma_p >= 0: load K block dma_kb into buffer dma_p meanwhile.
   // rd_p >= 0: read the fragments of stage half rd_h of buffer rd_p into
@@ -530,7 +543,7 @@ __device__ __forceinline__ void gemm_tile(
         if (rd_p >= 0 && item * DS_SPAN / DS_ITEMS == i) ds_item(rd_p, rd_h, item, na, nb);
 #pragma unroll
       for (int item = 0; item < DMA_ITEMS; ++item)
-        if (dma_p >= 0 && item * MFMAS / DMA_ITEMS == i) dma_item(dma_p, src, item);
+        if (dma_p >= 0 && item * DMA_SPAN / DMA_ITEMS == i) dma_item(dma_p, src, item);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
