@@ -22,7 +22,9 @@ mx_gemm), f32sfprop1p5b (the forward with fp32 instead of power-of-two scales),
 dualq (the two-orientation quantizers), gaussws7b (GaussWS sampling of the 7B
 weight from fp32 master weights), mxstress (MX quantization with clamp counts of
 64 distinct 4096x4096 fp32 tensors, with the clamp statistics).  gemmsweep times
-the GEMM alone over N and K; copy times a plain 256 MiB device copy.
+the GEMM alone over N and K; vendorgemm times the GEMM beside the FP8 products
+of the ROCm BLAS library (torch._scaled_mm) on the same shapes; copy times a
+plain 256 MiB device copy.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
                        [--cpu-rows R]
@@ -41,7 +43,7 @@ FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, TFLOP/s
 METRIC = "FP8 quantize GB/s + block-scaled FP8 GEMM TFLOP/s, % of MI355X peak"
 HERE = os.path.dirname(os.path.abspath(__file__))
 WORKLOADS = ["dgrad7b", "fprop1p5b", "wgrad", "mxfprop1p5b", "f32sfprop1p5b", "dualq", "gaussws7b", "mxstress",
-             "copy", "gemmsweep"]
+             "copy", "gemmsweep", "vendorgemm"]
 
 
 def parse():
@@ -870,6 +872,92 @@ def bench_gemm_sweep(args):
             "cpu_baseline": None}
 
 
+def bench_vendor_gemm(args):
+    """This library's GEMMs beside the ROCm BLAS library's FP8 products (torch._scaled_mm,
+    which dispatches to hipBLASLt) on the dgrad7b, fprop1p5b and wgrad shapes: per-tensor
+    scales (the least work: one scale for each operand), per-row/per-column scales, and
+    32-element E8M0 (MX) scales, against this library's 128x128-block and MX GEMMs.  Both
+    sides read the same E4M3 codes (a bf16 N(0, 1/4) draw cast to E4M3, B stored [N][K])
+    with unit scales, so every variant computes the same product; bf16 output.  Each
+    variant is timed over `steps` calls back to back between one event pair, in three
+    interleaved rounds (the median is kept), after a clock ramp.  A variant that the
+    library rejects is reported with its error text."""
+    import torch
+    import mx_block_scaled_x128_amd as mx
+    shapes = [("dgrad7b", 8192, 3584, 18944), ("fprop1p5b", 4096, 8960, 1536), ("wgrad", 4096, 4096, 16384)]
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    res = []
+    for name, M, N, K in shapes:
+        a = (torch.randn(M, K, device="cuda", generator=gen) * 0.5).to(torch.float8_e4m3fn)
+        bt = (torch.randn(N, K, device="cuda", generator=gen) * 0.5).to(torch.float8_e4m3fn)
+        au, bu = a.view(torch.uint8), bt.view(torch.uint8)
+        one = torch.ones((), device="cuda")
+        rows, cols = torch.ones(M, 1, device="cuda"), torch.ones(1, N, device="cuda")
+        mxa = torch.full((M, K // 32), 127, dtype=torch.uint8, device="cuda")
+        mxb = torch.full((N, K // 32), 127, dtype=torch.uint8, device="cuda")
+        sa = torch.full((M, K // 128), 127, dtype=torch.uint8, device="cuda")
+        sb = torch.full(((N + 127) // 128, K // 128), 127, dtype=torch.uint8, device="cuda")
+        out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        variants = {
+            "this: 128x128-block scales": lambda: mx.block_scaled_gemm(au, sa, mx.E4M3, bu, sb, mx.E4M3, mx.B_NK,
+                                                                       mx.SCALE_BLOCK128, out=out),
+            "this: MX scales": lambda: mx.mx_scaled_gemm(au, mxa, mx.E4M3, bu, mxb, mx.E4M3, out=out),
+            "hipBLASLt: per-tensor scales": lambda: torch._scaled_mm(a, bt.t(), scale_a=one, scale_b=one,
+                                                                     out_dtype=torch.bfloat16),
+            "hipBLASLt: per-row/column scales": lambda: torch._scaled_mm(a, bt.t(), scale_a=rows, scale_b=cols,
+                                                                         out_dtype=torch.bfloat16),
+            "hipBLASLt: MX scales": lambda: torch._scaled_mm(a, bt.t(), scale_a=mxa.view(torch.float8_e8m0fnu),
+                                                             scale_b=mxb.view(torch.float8_e8m0fnu),
+                                                             out_dtype=torch.bfloat16),
+        }
+        errors, times = {}, {k: [] for k in variants}
+        ref = None
+        for k, f in list(variants.items()):
+            try:
+                y = f()
+                torch.cuda.synchronize()
+                y = out if y is None else y
+                if ref is None:
+                    ref = y.float().clone()
+                elif not torch.allclose(y.float(), ref, rtol=2 ** -7, atol=1e-2 * float(ref.abs().max())):
+                    errors[k] = "output differs from this library's block-scaled product"
+            except Exception as e:  # a scaling mode the installed library does not offer
+                errors[k] = str(e).splitlines()[0][:160]
+                del variants[k]
+        ramp(lambda timer: variants["this: 128x128-block scales"](), 0.3)
+        for _ in range(3):
+            for k, f in variants.items():
+                for _ in range(args.warmup):
+                    f()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(args.steps):
+                    f()
+                e1.record()
+                torch.cuda.synchronize()
+                times[k].append(e0.elapsed_time(e1) * 1e3 / args.steps)
+        for k in times:
+            if times[k]:
+                us = float(np.median(times[k]))
+                res.append({"shape": name, "M": M, "N": N, "K": K, "gemm": k, "us": round(us, 2),
+                            "TFLOP/s": round(2.0 * M * N * K / us / 1e6, 1)})
+            if k in errors:
+                res.append({"shape": name, "M": M, "N": N, "K": K, "gemm": k, "error": errors[k]})
+        del a, bt, au, bu, mxa, mxb, sa, sb, out, ref, variants
+    main_line = [r for r in res if r["shape"] == "dgrad7b" and r["gemm"] == "this: 128x128-block scales"][0]
+    return {"metric": "FP8 GEMM TFLOP/s beside the ROCm BLAS library's FP8 products", "value": main_line["TFLOP/s"],
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(main_line["us"] / 1e3, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic (bf16 N(0, 1/4) cast to E4M3, unit scales)",
+            "config": {"workload": "vendorgemm: dgrad7b 8192x3584x18944, fprop1p5b 4096x8960x1536, "
+                                   "wgrad 4096x4096x16384"},
+            "comparison": res,
+            "roofline": {"bound": "mfma", "achieved": main_line["TFLOP/s"], "peak": FP8_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(main_line["TFLOP/s"] / FP8_PEAK_TFLOPS, 4), "traffic": None},
+            "cpu_baseline": None}
+
+
 def bench_copy(args):
     """A plain device copy of 256 MiB (torch's copy kernel): the reference point that scales
     profiler byte counters (FETCH_SIZE / WRITE_SIZE) to bytes, and a measured bandwidth."""
@@ -902,6 +990,8 @@ def main():
         line = bench_copy(args)
     elif args.workload == "gemmsweep":
         line = bench_gemm_sweep(args)
+    elif args.workload == "vendorgemm":
+        line = bench_vendor_gemm(args)
     else:
         line = bench_workload(args)
     print(json.dumps(line), flush=True)

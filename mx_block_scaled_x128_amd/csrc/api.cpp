@@ -101,7 +101,7 @@ int fp8_quantize_block_f32s(const void* w, int w_dtype, int64_t rows, int64_t co
 namespace {
 // Checks shared by the two-orientation quantizers: both output pairs as for
 // the one-orientation calls, both extents multiples of 16, four distinct outputs.
-int check_dual(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt, const uint8_t* q,
+static int check_dual(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt, const uint8_t* q,
                int64_t ldq, const uint8_t* s, const uint8_t* qt, int64_t ldqt, const uint8_t* st) {
   if (fmt != MXFP8_E4M3 && fmt != MXFP8_E5M2) return MXFP8_ERR_ENUM;
   int r = check_tensor_pair(x, dtype, rows, cols, ldx, q, ldq, cols, s);

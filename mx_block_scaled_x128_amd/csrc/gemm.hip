@@ -38,9 +38,32 @@
 
 #include <atomic>
 
+// One translation unit can hold every kernel (MXFP8_GEMM_FMT undefined), or
+// the build compiles this file once per (A format, B format) pair,
+// MXFP8_GEMM_FMT = 2 * a_fmt + b_fmt, in parallel, plus once with
+// MXFP8_GEMM_FMT = -1 for the host dispatch alone.
+#ifndef MXFP8_GEMM_FMT
+#define MXFP8_GEMM_FMT 4
+#endif
+
 namespace mxfp8 {
 
 namespace gemm_detail {
+
+template <int AFMT, int BFMT>
+void launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
+                const uint8_t* b, int64_t ldb, int b_layout, const uint8_t* sb, int b_scale_mode, void* c,
+                int64_t ldc, int c_dtype, hipStream_t stream);
+template <int AFMT, int BFMT>
+void launch_f32s_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
+                     const uint8_t* b, int64_t ldb, int b_layout, const uint8_t* sb, int b_scale_mode, void* c,
+                     int64_t ldc, int c_dtype, hipStream_t stream);
+template <int AFMT, int BFMT>
+void launch_mx_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
+                   const uint8_t* b, int64_t ldb, const uint8_t* sb, void* c, int64_t ldc, int c_dtype,
+                   hipStream_t stream);
+
+#if MXFP8_GEMM_FMT >= 0
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -166,7 +189,7 @@ struct TileLds {
 // launch); the kernels below host it on their own LDS arrays (kbuf0, kbuf1:
 // TileLds::PB bytes each, sgrp: TileLds::SGRP bytes, all 1024-byte aligned),
 // one array per buffer so that every access names its buffer.
-template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool F32S>
+template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool F32S, bool WS>
 __device__ __forceinline__ void gemm_tile(
     int M, int N, int K, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ SA,
     const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ SB, void* __restrict__ C,
@@ -195,12 +218,31 @@ __device__ __forceinline__ void gemm_tile(
   static_assert(BM <= kThreads && BN <= kThreads, "one scale entity per lane quarter");
   static_assert(A_LOADS + B_LOADS + 8 <= 63, "vmcnt range");
   // Scale groups: the scales of 4 consecutive K blocks for each of 256 tile
-  // rows (A) and columns (B), double-buffered.  Dword d = 4 e + s of a group
-  // area holds entity e's scale for K block 4g + s: one byte, zero-extended
-  // (the LDS layout of 1-byte LDS-bound loads), or with MXS the four 32-wide
-  // block scales of that K block (one 4-byte load).  Loading 4 K blocks
-  // at a time touches each row's scale line once per 4 K blocks instead of
-  // once per K block (rows are nkb bytes apart in [rows][K/128] scales).
+  // rows (A) and columns (B), double-buffered.  Loading 4 K blocks at a time
+  // touches each row's scale line once per 4 K blocks instead of once per K
+  // block (rows are nkb bytes apart in [rows][K/128] scales).  A 1-byte
+  // LDS-bound load writes each lane's byte zero-extended into its own dword;
+  // a 4-byte one writes the lane's 4 bytes.  An operand's group area holds
+  // one of three layouts:
+  //  * rows: scales per row of the operand's [rows][K] storage (A; B with
+  //    per-row or MX scales).  Entity e's K block 4g + s in the dword at
+  //    16 e + 4 s (MXS: that K block's four 32-wide block scales).  Loads:
+  //    instruction q = 4 wave + j covers e = 16 q + lane / 4, s = lane % 4.
+  //  * wide rows (WS: one E8M0 byte per K block, K blocks a multiple of 4,
+  //    scale arrays 4-byte aligned): entity e's four bytes (s = 0..3) in the
+  //    dword at 4 e, one 4-byte load per lane (entity 64 wave + lane), one
+  //    instruction per operand and wave instead of four, and the 32 rows of
+  //    a fragment read 32 consecutive dwords (no bank conflicts; the rows
+  //    layout's 16-byte stride costs ~10 conflict cycles per read).
+  //  * blocks: B scales per 128 x 128 block of its storage.  A tile's columns
+  //    span at most two scale blocks, n0 / 128 + c (c = 0, 1), and each wave's
+  //    columns lie in one of them, c = wn * WN / 128.  Each wave loads the
+  //    group's 8 values into its own 256-byte row, (K block s, block c) in
+  //    dword 2 s + c (lanes 8..63 repeat lanes 0..7), and reads its value with
+  //    one same-address (broadcast) read per K block.  One instruction per
+  //    wave instead of four.
+  constexpr bool B_ROWS = BROW || MXS;
+  static_assert(!WS || (!MXS && !F32S), "wide scale loads: one E8M0 byte per K block");
   constexpr int SG_OP = kThreads * 4 * 4;            // one operand's group area (bytes)
   constexpr int SG = 2 * SG_OP;                      // A then B
   static_assert(2 * SG == TileLds<BM, BN>::SGRP, "scale group areas");
@@ -272,46 +314,56 @@ __device__ __forceinline__ void gemm_tile(
   }
   const int64_t b_step = BKN ? (int64_t)KBB * ldb : KBB;
 
-  // Scale sources.  Group g's load instruction j of a wave (4 per operand)
-  // covers entities e = 16 (4 wave + j) + (lane >> 2), K block 4g + (lane & 3)
-  // (clamped to the last one; rows past M / N are clamped too).
+  // Scale sources of group grp (layouts above).  K blocks past the last one
+  // and rows past M / N are clamped to the last ones.
   const int srow = (MXS || F32S) ? 4 * nkb : nkb;  // scale bytes per row of A (and of per-row B scales)
   const uint8_t* sa_base = uniform_opaque(SA + (int64_t)m0 * srow);
   const uint8_t* sb_base = uniform_opaque(BROW ? SB + (int64_t)n0 * srow : SB);
   auto sdma_group = [&](int grp) __attribute__((always_inline)) {
     uint8_t* area = sgrp + (grp & 1) * SG;
-    const int kbs = min(4 * grp + (lane & 3), nkb - 1);
+    if constexpr (WS) {
+      const int e = wave * 64 + lane;
+      const int kb4 = 4 * min(grp, (nkb >> 2) - 1);
+      __builtin_amdgcn_global_load_lds(sa_base + (uint32_t)(min(e, M - 1 - m0) * nkb + kb4), area + wave * 256, 4,
+                                       0, 0);
+      if constexpr (BROW)
+        __builtin_amdgcn_global_load_lds(sb_base + (uint32_t)(min(e, N - 1 - n0) * nkb + kb4),
+                                         area + SG_OP + wave * 256, 4, 0, 0);
+    } else {
+      const int kbs = min(4 * grp + (lane & 3), nkb - 1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = (wave * 4 + j) * 16 + (lane >> 2);
-      if (MXS || F32S) {
-        const uint32_t off = (uint32_t)(min(e, M - 1 - m0) * srow + 4 * kbs);
-        __builtin_amdgcn_global_load_lds(sa_base + off, area + (wave * 4 + j) * 256, 4, 0, 0);
-      } else {
-        const uint32_t off = (uint32_t)(min(e, M - 1 - m0) * nkb + kbs);
-        __builtin_amdgcn_global_load_lds(sa_base + off, area + (wave * 4 + j) * 256, 1, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const int e = (wave * 4 + j) * 16 + (lane >> 2);
+        if (MXS || F32S) {
+          const uint32_t off = (uint32_t)(min(e, M - 1 - m0) * srow + 4 * kbs);
+          __builtin_amdgcn_global_load_lds(sa_base + off, area + (wave * 4 + j) * 256, 4, 0, 0);
+        } else {
+          const uint32_t off = (uint32_t)(min(e, M - 1 - m0) * nkb + kbs);
+          __builtin_amdgcn_global_load_lds(sa_base + off, area + (wave * 4 + j) * 256, 1, 0, 0);
+        }
+      }
+      if constexpr (B_ROWS) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = (wave * 4 + j) * 16 + (lane >> 2);
+          if constexpr (MXS || F32S) {
+            const uint32_t off = (uint32_t)(min(e, N - 1 - n0) * srow + 4 * kbs);
+            __builtin_amdgcn_global_load_lds(sb_base + off, area + SG_OP + (wave * 4 + j) * 256, 4, 0, 0);
+          } else {
+            const uint32_t off = (uint32_t)(min(e, N - 1 - n0) * nkb + kbs);
+            __builtin_amdgcn_global_load_lds(sb_base + off, area + SG_OP + (wave * 4 + j) * 256, 1, 0, 0);
+          }
+        }
       }
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = (wave * 4 + j) * 16 + (lane >> 2);
-      if (MXS || (F32S && BROW)) {
-        const uint32_t off = (uint32_t)(min(e, N - 1 - n0) * srow + 4 * kbs);
-        __builtin_amdgcn_global_load_lds(sb_base + off, area + SG_OP + (wave * 4 + j) * 256, 4, 0, 0);
-      } else if (F32S) {
-        const int nb = min((n0 + e) >> 7, nnb - 1);
-        const uint32_t off = (uint32_t)(4 * (BKN ? kbs * nnb + nb : nb * nkb + kbs));
-        __builtin_amdgcn_global_load_lds(sb_base + off, area + SG_OP + (wave * 4 + j) * 256, 4, 0, 0);
-      } else {
-        uint32_t off;
-        if (BROW) {
-          off = (uint32_t)(min(e, N - 1 - n0) * nkb + kbs);
-        } else {
-          const int nb = min((n0 + e) >> 7, nnb - 1);
-          off = (uint32_t)(BKN ? kbs * nnb + nb : nb * nkb + kbs);
-        }
-        __builtin_amdgcn_global_load_lds(sb_base + off, area + SG_OP + (wave * 4 + j) * 256, 1, 0, 0);
-      }
+    if constexpr (!B_ROWS) {
+      const int kbs = min(4 * grp + ((lane & 7) >> 1), nkb - 1);
+      const int nb = min((n0 >> 7) + (lane & 1), nnb - 1);
+      const uint32_t idx = (uint32_t)(BKN ? kbs * nnb + nb : nb * nkb + kbs);
+      if constexpr (F32S)
+        __builtin_amdgcn_global_load_lds(sb_base + 4 * idx, area + SG_OP + wave * 256, 4, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(sb_base + idx, area + SG_OP + wave * 256, 1, 0, 0);
     }
   };
 
@@ -351,28 +403,38 @@ __device__ __forceinline__ void gemm_tile(
   // Scale operands of K block kb (from its group's area).  With MXS, lane
   // half g reads the 32-wide block scales 2g and 2g+1 of the K block (the
   // chunks whose scale it supplies in the block's two stages, see below);
-  // stage h selects byte h with the MFMA's operand select.
+  // stage h selects byte h with the MFMA's operand select.  Fragment mt's
+  // rows are entities wm * WM + 32 mt + lane % 32 (likewise for B columns).
   const int g = lane >> 5;
-  const uint32_t sa_rd = opaque((wm * WM + (lane & 31)) * 16 + (MXS ? 2 * g : 0));
-  const uint32_t sb_rd = opaque(SG_OP + (wn * WN + (lane & 31)) * 16 + (MXS ? 2 * g : 0));
+  constexpr int ROW_E = WS ? 4 : 16;                 // bytes per entity in a rows layout
+  const uint32_t sa_rd = opaque(ROW_E * (wm * WM + (lane & 31)) + (MXS ? 2 * g : 0));
+  const uint32_t sb_rd = opaque(SG_OP + (B_ROWS ? ROW_E * (wn * WN + (lane & 31)) + (MXS ? 2 * g : 0)
+                                                : wave * 256 + 4 * ((wn * WN) >> 7)));
   // With F32S and per-column B scales, lane half g reads the scales of its
   // 16 accumulator columns 8q + 4g + j (q, j = 0..3) of each fragment.
-  const uint32_t sbc_rd = opaque(SG_OP + (wn * WN + 4 * g) * 16);
+  const uint32_t sbc_rd = opaque(SG_OP + 16 * (wn * WN + 4 * g));
+  auto read_scale = [&](const uint8_t* p, bool byte) __attribute__((always_inline)) -> int {
+    if (byte) return (int)*p;
+    if (MXS) return (int)*reinterpret_cast<const uint16_t*>(p);
+    return *reinterpret_cast<const int*>(p);
+  };
   auto read_scales = [&](int kb, int (&sa)[MT], int (&sb)[NT * SBP]) __attribute__((always_inline)) {
-    const uint8_t* area = sgrp + ((kb >> 2) & 1) * SG + (kb & 3) * 4;
+    const uint8_t* area = sgrp + ((kb >> 2) & 1) * SG;
+    const int ks = kb & 3;
+    const uint8_t* ar = area + (WS ? ks : 4 * ks);
+    const uint8_t* br = area + (B_ROWS ? (WS ? ks : 4 * ks) : 8 * ks);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      sa[mt] = MXS ? (int)*reinterpret_cast<const uint16_t*>(area + sa_rd + mt * 512)
-                   : *reinterpret_cast<const int*>(area + sa_rd + mt * 512);
+    for (int mt = 0; mt < MT; ++mt) sa[mt] = read_scale(ar + sa_rd + mt * 32 * ROW_E, WS);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       if constexpr (SBP == 16) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          sb[nt * 16 + r] = *reinterpret_cast<const int*>(area + sbc_rd + (nt * 32 + 8 * (r >> 2) + (r & 3)) * 16);
+          sb[nt * 16 + r] = *reinterpret_cast<const int*>(br + sbc_rd + 16 * (nt * 32 + 8 * (r >> 2) + (r & 3)));
+      } else if constexpr (B_ROWS) {
+        sb[nt] = read_scale(br + sb_rd + nt * 32 * ROW_E, WS);
       } else {
-        sb[nt] = MXS ? (int)*reinterpret_cast<const uint16_t*>(area + sb_rd + nt * 512)
-                     : *reinterpret_cast<const int*>(area + sb_rd + nt * 512);
+        sb[nt] = nt == 0 ? *reinterpret_cast<const int*>(br + sb_rd) : sb[0];  // one block per wave
       }
     }
   };
@@ -568,12 +630,11 @@ __device__ __forceinline__ void gemm_tile(
   // fragments and scales.  One barrier per K block.
   // kblock(p, kb, ...): K block kb in buffer p with scale set (csa, csb);
   // dma: load K block kb+2; next: kb+1 exists (read its scales into (nsa, nsb)).
-  // sg: also load scale group (kb >> 2) + 1 (kb even, in the main loop's
-  // first K block of each pair).  At kb = 0 mod 4 that group first lands in
-  // its area, whose previous group was last read one K block earlier; at
-  // kb = 2 mod 4 the same bytes are written again (harmless, and no branch
-  // in the instruction stream); a group past the last K block loads clamped
-  // bytes nobody reads.  A group is read from 2 to 3 K blocks later on.
+  // sg: also load scale group (kb >> 2) + 1 (kb = 0 mod 4: the first K block
+  // of each four, and of a trailing pair).  The group lands in its area,
+  // whose previous group was last read one K block earlier; a group past the
+  // last K block loads clamped bytes nobody reads.  A group is read from 3 to
+  // 6 K blocks later on.
   auto kblock = [&](int p, int kb, bool dma, bool next, bool sg, const int (&csa)[MT], const int (&csb)[NT * SBP],
                     int (&nsa)[MT], int (&nsb)[NT * SBP]) __attribute__((always_inline)) {
     stage(0, -1, 0, p, 1, false, 0, -1, fa0, fb0, fa1, fb1, csa, csb, nsa, nsb);
@@ -598,16 +659,25 @@ __device__ __forceinline__ void gemm_tile(
   }
 
   // ---- steady state: K blocks whose second stage loads a later block, in
-  // pairs, then a lone one if their count is odd.  The loop body names its
+  // fours (one scale group load each: a loop of pairs loading the group in
+  // every pair spent 10 % more load instructions and ran 1-3 % slower), then
+  // a pair and a lone one as their count needs.  The loop body names its
   // buffers as constants and every path into the loop has the same loads in
   // flight, so the compiler's per-buffer tracking of in-flight LDS-bound
   // loads stays exact around it.
   const int main_kb = nkb - 2;  // K blocks whose second stage loads a later block
   int kb = 0;
 #pragma nounroll
-  for (; kb + 1 < main_kb; kb += 2) {  // two K blocks: buffers 0, 1; scale sets 0, 1
+  for (; kb + 3 < main_kb; kb += 4) {  // four K blocks: buffers 0, 1, 0, 1; scale sets 0, 1, 0, 1
     kblock(0, kb, true, true, true, sa0, sb0, sa1, sb1);
     kblock(1, kb + 1, true, true, false, sa1, sb1, sa0, sb0);
+    kblock(0, kb + 2, true, true, false, sa0, sb0, sa1, sb1);
+    kblock(1, kb + 3, true, true, false, sa1, sb1, sa0, sb0);
+  }
+  if (kb + 1 < main_kb) {
+    kblock(0, kb, true, true, true, sa0, sb0, sa1, sb1);
+    kblock(1, kb + 1, true, true, false, sa1, sb1, sa0, sb0);
+    kb += 2;
   }
   if (kb < main_kb) {
     kblock(0, kb, true, true, false, sa0, sb0, sa1, sb1);
@@ -758,7 +828,7 @@ __device__ __forceinline__ void gemm_tile(
 #endif
 }
 
-template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool F32S>
+template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool F32S, bool WS>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ SA,
     const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ SB, void* __restrict__ C,
@@ -768,9 +838,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[L::PB];
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[L::PB];
   __shared__ __attribute__((aligned(1024))) uint8_t sgrp[L::SGRP];
-  gemm_tile<BM, BN, STAGES, AFMT, BFMT, BKN, BROW, MXS, F32S>(M, N, K, A, lda, SA, B, ldb, SB, C, ldc, out_bf16,
-                                                             tiles_m, tiles_n, tile_first, 0, 0, blockIdx.x,
-                                                             gridDim.x, kbuf0, kbuf1, sgrp);
+  gemm_tile<BM, BN, STAGES, AFMT, BFMT, BKN, BROW, MXS, F32S, WS>(M, N, K, A, lda, SA, B, ldb, SB, C, ldc,
+                                                                 out_bf16, tiles_m, tiles_n, tile_first, 0, 0,
+                                                                 blockIdx.x, gridDim.x, kbuf0, kbuf1, sgrp);
 #endif
 }
 
@@ -784,7 +854,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
 // halves instead of quadrants, half as many workgroups, took 3 us longer on
 // the 4096x8960x1536 shape.)
 constexpr int kTailSub = 4;
-template <int AFMT, int BFMT, bool BKN, bool BROW, bool MXS>
+template <int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool WS>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bs_split_tail_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ SA,
     const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ SB, void* __restrict__ C,
@@ -797,29 +867,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_split_tail_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t sgrp[L::SGRP];
   const int b = blockIdx.x;
   if (b < big)
-    gemm_tile<256, 256, 4, AFMT, BFMT, BKN, BROW, MXS, false>(M, N, K, A, lda, SA, B, ldb, SB, C, ldc, out_bf16,
-                                                              tiles_m, tiles_n, 0, 0, 0, b, big, kbuf0, kbuf1,
-                                                              sgrp);
+    gemm_tile<256, 256, 4, AFMT, BFMT, BKN, BROW, MXS, false, WS>(M, N, K, A, lda, SA, B, ldb, SB, C, ldc,
+                                                                  out_bf16, tiles_m, tiles_n, 0, 0, 0, b, big, kbuf0,
+                                                                  kbuf1, sgrp);
   else
-    gemm_tile<128, 128, 4, AFMT, BFMT, BKN, BROW, MXS, false>(M, N, K, A, lda, SA, B, ldb, SB, C, ldc, out_bf16,
-                                                              tiles_m, tiles_n, big, 1, 1, b - big,
-                                                              (int)gridDim.x - big, kbuf0, kbuf1, sgrp);
+    gemm_tile<128, 128, 4, AFMT, BFMT, BKN, BROW, MXS, false, WS>(M, N, K, A, lda, SA, B, ldb, SB, C, ldc,
+                                                                  out_bf16, tiles_m, tiles_n, big, 1, 1, b - big,
+                                                                  (int)gridDim.x - big, kbuf0, kbuf1, sgrp);
 #endif
 }
 
-template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool F32S = false>
+template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool F32S, bool WS>
 void launch_tile(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
                  const uint8_t* b, int64_t ldb, const uint8_t* sb, void* c, int64_t ldc, int c_dtype,
                  int tiles_m, int tiles_n, int tile_first, int cells, hipStream_t stream) {
   if (cells <= 0) return;
-  hipLaunchKernelGGL((gemm_bs_kernel<BM, BN, STAGES, AFMT, BFMT, BKN, BROW, MXS, F32S>), dim3(cells),
+  hipLaunchKernelGGL((gemm_bs_kernel<BM, BN, STAGES, AFMT, BFMT, BKN, BROW, MXS, F32S, WS>), dim3(cells),
                      dim3(kThreads), 0, stream, (int)M, (int)N, (int)K, a, lda, sa, b, ldb, sb, c, ldc,
                      c_dtype == 1 ? 1 : 0, tiles_m, tiles_n, tile_first);
 }
 
 // Compute units of the current device (cached per device; concurrent first
 // calls store the same value).
-int device_cus() {
+inline int device_cus() {
   static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -838,7 +908,7 @@ int device_cus() {
 #ifndef MXFP8_GEMM_TILE
 #define MXFP8_GEMM_TILE 0
 #endif
-template <int AFMT, int BFMT, bool BKN, bool BROW, bool MXS>
+template <int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool WS>
 void launch_shape(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
                   const uint8_t* b, int64_t ldb, const uint8_t* sb, void* c, int64_t ldc, int c_dtype,
                   hipStream_t stream) {
@@ -849,8 +919,8 @@ void launch_shape(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda
   const bool big = K >= 256 && (MXFP8_GEMM_TILE == 256 || (MXFP8_GEMM_TILE == 0 && big_tiles >= cus));
   if (!big) {
     const int sm = (int)((M + 127) / 128), sn = (int)((N + 127) / 128);
-    launch_tile<128, 128, 4, AFMT, BFMT, BKN, BROW, MXS>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, sm, sn, 0,
-                                                    sm * sn, stream);
+    launch_tile<128, 128, 4, AFMT, BFMT, BKN, BROW, MXS, false, WS>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype,
+                                                                   sm, sn, 0, sm * sn, stream);
     return;
   }
   // Last partial round: when its 256x256 tiles, cut in kTailSub, fit on the
@@ -858,14 +928,14 @@ void launch_shape(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda
   const int tail = big_tiles % cus;
   const bool split_tail = MXFP8_GEMM_TILE == 0 && big_tiles > cus && tail > 0 && kTailSub * tail <= cus;
   if (!split_tail) {
-    launch_tile<256, 256, 4, AFMT, BFMT, BKN, BROW, MXS>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, bm, bn,
-                                                    0, big_tiles, stream);
+    launch_tile<256, 256, 4, AFMT, BFMT, BKN, BROW, MXS, false, WS>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype,
+                                                                   bm, bn, 0, big_tiles, stream);
     return;
   }
   // main_cells is a multiple of the CU count (256 = 8 XCDs x 32), so both
   // parts of the launch keep their per-XCD bands.
   const int main_cells = big_tiles - tail;
-  hipLaunchKernelGGL((gemm_bs_split_tail_kernel<AFMT, BFMT, BKN, BROW, MXS>), dim3(main_cells + kTailSub * tail),
+  hipLaunchKernelGGL((gemm_bs_split_tail_kernel<AFMT, BFMT, BKN, BROW, MXS, WS>), dim3(main_cells + kTailSub * tail),
                      dim3(kThreads), 0, stream, (int)M, (int)N, (int)K, a, lda, sa, b, ldb, sb, c, ldc,
                      c_dtype == 1 ? 1 : 0, bm, bn, main_cells);
 }
@@ -874,12 +944,22 @@ template <int AFMT, int BFMT>
 void launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
                 const uint8_t* b, int64_t ldb, int b_layout, const uint8_t* sb, int b_scale_mode, void* c,
                 int64_t ldc, int c_dtype, hipStream_t stream) {
+  // Wide scale loads (one 4-byte load per row for 4 K blocks) need 4-byte
+  // aligned rows: K blocks a multiple of 4 and 4-byte aligned row scales.
+  const int64_t nkb = K / 128;
+  const bool brow = b_layout == 0 && b_scale_mode == 1;
+  const bool ws = nkb >= 4 && nkb % 4 == 0 && reinterpret_cast<uintptr_t>(sa) % 4 == 0 &&
+                  (!brow || reinterpret_cast<uintptr_t>(sb) % 4 == 0);
+#define MXFP8_SHAPE(BKN, BROW)                                                                                \
+  (ws ? launch_shape<AFMT, BFMT, BKN, BROW, false, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream) \
+      : launch_shape<AFMT, BFMT, BKN, BROW, false, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream))
   if (b_layout == 1)
-    launch_shape<AFMT, BFMT, true, false, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
-  else if (b_scale_mode == 1)
-    launch_shape<AFMT, BFMT, false, true, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+    MXFP8_SHAPE(true, false);
+  else if (brow)
+    MXFP8_SHAPE(false, true);
   else
-    launch_shape<AFMT, BFMT, false, false, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+    MXFP8_SHAPE(false, false);
+#undef MXFP8_SHAPE
 }
 
 // fp32 block scales: 128x128 tiles only (the temporaries double the
@@ -890,19 +970,49 @@ void launch_f32s_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t 
                      int64_t ldc, int c_dtype, hipStream_t stream) {
   const int sm = (int)((M + 127) / 128), sn = (int)((N + 127) / 128);
   if (b_layout == 1)
-    launch_tile<128, 128, 4, AFMT, BFMT, true, false, false, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype,
+    launch_tile<128, 128, 4, AFMT, BFMT, true, false, false, true, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype,
                                                                   sm, sn, 0, sm * sn, stream);
   else if (b_scale_mode == 1)
-    launch_tile<128, 128, 4, AFMT, BFMT, false, true, false, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype,
+    launch_tile<128, 128, 4, AFMT, BFMT, false, true, false, true, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype,
                                                                   sm, sn, 0, sm * sn, stream);
   else
-    launch_tile<128, 128, 4, AFMT, BFMT, false, false, false, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc,
+    launch_tile<128, 128, 4, AFMT, BFMT, false, false, false, true, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc,
                                                                    c_dtype, sm, sn, 0, sm * sn, stream);
 }
+
+template <int AFMT, int BFMT>
+void launch_mx_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
+                   const uint8_t* b, int64_t ldb, const uint8_t* sb, void* c, int64_t ldc, int c_dtype,
+                   hipStream_t stream) {
+  launch_shape<AFMT, BFMT, false, true, true, false>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+}
+
+#define MXFP8_GEMM_PAIR(AF, BF)                                                                                   \
+  template void launch_fmt<AF, BF>(int64_t, int64_t, int64_t, const uint8_t*, int64_t, const uint8_t*,            \
+                                   const uint8_t*, int64_t, int, const uint8_t*, int, void*, int64_t, int,         \
+                                   hipStream_t);                                                                   \
+  template void launch_f32s_fmt<AF, BF>(int64_t, int64_t, int64_t, const uint8_t*, int64_t, const uint8_t*,       \
+                                        const uint8_t*, int64_t, int, const uint8_t*, int, void*, int64_t, int,    \
+                                        hipStream_t);                                                              \
+  template void launch_mx_fmt<AF, BF>(int64_t, int64_t, int64_t, const uint8_t*, int64_t, const uint8_t*,         \
+                                      const uint8_t*, int64_t, const uint8_t*, void*, int64_t, int, hipStream_t);
+#if MXFP8_GEMM_FMT == 4
+MXFP8_GEMM_PAIR(0, 0)
+MXFP8_GEMM_PAIR(1, 0)
+MXFP8_GEMM_PAIR(0, 1)
+MXFP8_GEMM_PAIR(1, 1)
+#else
+MXFP8_GEMM_PAIR((MXFP8_GEMM_FMT >> 1), (MXFP8_GEMM_FMT & 1))
+#endif
+#undef MXFP8_GEMM_PAIR
+
+#endif  // MXFP8_GEMM_FMT >= 0
 
 }  // namespace gemm_detail
 
 using namespace gemm_detail;
+
+#if MXFP8_GEMM_FMT == 4 || MXFP8_GEMM_FMT < 0
 
 void launch_gemm_f32s(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, int a_fmt,
                       const float* sa, const uint8_t* b, int64_t ldb, int b_fmt, int b_layout, const float* sb,
@@ -937,13 +1047,15 @@ void launch_mx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t l
                     const uint8_t* sa, const uint8_t* b, int64_t ldb, int b_fmt, const uint8_t* sb, void* c,
                     int64_t ldc, int c_dtype, hipStream_t stream) {
   if (a_fmt == 0 && b_fmt == 0)
-    launch_shape<0, 0, false, true, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+    launch_mx_fmt<0, 0>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
   else if (a_fmt == 1 && b_fmt == 0)
-    launch_shape<1, 0, false, true, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+    launch_mx_fmt<1, 0>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
   else if (a_fmt == 0 && b_fmt == 1)
-    launch_shape<0, 1, false, true, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+    launch_mx_fmt<0, 1>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
   else
-    launch_shape<1, 1, false, true, true>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
+    launch_mx_fmt<1, 1>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype, stream);
 }
+
+#endif  // host dispatch
 
 }  // namespace mxfp8

@@ -510,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(
   }
 }
 
-uint32_t grid_for(uint64_t items, int per_wave) {
+static uint32_t grid_for(uint64_t items, int per_wave) {
   const uint64_t waves = (items + per_wave - 1) / per_wave;
   uint64_t blocks = (waves + 3) / 4;
   if (blocks > kMaxBlocks) blocks = kMaxBlocks;
