@@ -52,14 +52,15 @@ def test_outer_products_of_every_code_pair_exact(a_fmt, b_fmt, b_layout, kpos):
 
 @pytest.mark.parametrize("a_fmt,b_fmt", FMT_PAIRS)
 @pytest.mark.parametrize("b_layout", [mx.B_NK, mx.B_KN])
-@pytest.mark.parametrize("kpos", [5, 700, 762])
-def test_outer_products_on_the_256_tile_exact(a_fmt, b_fmt, b_layout, kpos):
+@pytest.mark.parametrize("K,kpos", [(768, 5), (768, 700), (768, 762), (1024, 5), (1024, 900), (1024, 1018)])
+def test_outer_products_on_the_256_tile_exact(a_fmt, b_fmt, b_layout, K, kpos):
     """The same exact products on the 256x256 tile path (4096 x 4096 output, one tile
-    per compute unit), K = 768: the code sits in the first K block, in the main loop's
-    last K block pair, or in the last stage of the drain (k = 762)."""
+    per compute unit).  K = 768 (6 K blocks: one 1-byte scale load per K block) and
+    K = 1024 (8 K blocks: one 4-byte load per row for 4 K blocks): the code sits in
+    the first K block, in the last K blocks of the main loop, or in the last stage of
+    the drain."""
     ca, cb = finite_codes(a_fmt), finite_codes(b_fmt)
     M = N = 4096
-    K = 768
     a, sa, b, sb = outer_product_operands(ca, cb, M, N, K, kpos, b_layout)
     y = run_gemm(a, sa, a_fmt, b, sb, b_fmt, b_layout, mx.SCALE_BLOCK128, False)
     va = oracle.decode(a_fmt, ca)[np.arange(M) % len(ca)]
@@ -220,6 +221,54 @@ def test_short_last_round_as_quadrants(b_layout, b_scale, bf16_out):
     y_s, t_s = oracle.gemm_elems(a, sa, 0, b, sb_store, 1, ii, jj, b_layout, b_scale, threads=8)
     hb_s = alignment_bound_fn(a, sa, 0, b_nk, sb, 1, b_scale, ii=ii, jj=jj)
     assert_gemm_close(y[ii, jj], y_s, t_s, bf16_out, "sampled", hw_bound=hb_s, max_over_plain=adversarial_cap(ii.size))
+
+
+def _at_odd_address(t):
+    """The same bytes, contiguous, starting one byte into an allocation."""
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    v = buf[1:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("b_layout,b_scale", [(mx.B_NK, mx.SCALE_BLOCK128), (mx.B_KN, mx.SCALE_BLOCK128),
+                                              (mx.B_NK, mx.SCALE_ROW128)])
+@pytest.mark.parametrize("M,N", [(4096, 4096), (4096 + 256, 4096), (640, 384)])
+def test_wide_and_byte_scale_loads_agree(b_layout, b_scale, M, N):
+    """K = 2048 (16 K blocks).  With 4-byte aligned row-scale arrays and a K-block
+    count that is a multiple of 4, the kernels fetch each row's scales for four K
+    blocks with one 4-byte load; a scale array at an odd address takes one 1-byte
+    load per K block.  Both must give the same bits -- on one round of 256x256 tiles,
+    on 17 x 16 cells whose last 16 run as 128x128 quadrants, and on 128x128 tiles --
+    and sampled outputs must meet the plain bound against the oracle.  Operands are
+    N(0, 1) data quantized on the GPU (1x128 rows for A and per-row B, 128x128
+    blocks otherwise)."""
+    K = 2048
+    rng = np.random.default_rng(900 + M + N + 10 * b_layout + b_scale)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    aq, a_s = mx.quantize_token(dev(x), mx.E4M3, mx.ROW)
+    if b_scale == mx.SCALE_ROW128:
+        bq, b_s = mx.quantize_token(dev(w), mx.E4M3, mx.ROW)
+    elif b_layout == mx.B_NK:
+        bq, b_s = mx.quantize_block(dev(w), mx.E4M3)
+    else:
+        bq, b_s = mx.quantize_block(dev(np.ascontiguousarray(w.T)), mx.E4M3)
+
+    def call(sa_t, sb_t):
+        return mx.block_scaled_gemm(aq, sa_t, mx.E4M3, bq, sb_t, mx.E4M3, b_layout, b_scale)
+    y = call(a_s, b_s)
+    others = [call(_at_odd_address(a_s), b_s)]
+    if b_scale == mx.SCALE_ROW128:
+        others.append(call(a_s, _at_odd_address(b_s)))
+    torch.cuda.synchronize()
+    for o in others:
+        assert torch.equal(y, o)
+    ii = rng.integers(0, M, 4096)
+    jj = rng.integers(0, N, 4096)
+    y_s, t_s = oracle.gemm_elems(host(aq), host(a_s), 0, host(bq), host(b_s), 0, ii, jj, b_layout, b_scale,
+                                 threads=8)
+    assert_gemm_close(host(y)[ii, jj], y_s, t_s, False, "wide scale loads")
 
 
 def _e4m3_code(v):
