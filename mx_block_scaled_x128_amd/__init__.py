@@ -178,20 +178,31 @@ def _check(status, where):
         raise MxFp8Error(status, where)
 
 
-def _require(cond, msg):
+def _require(cond, msg, *args):
+    """Raise ValueError(msg % args) unless cond; the message is formatted only then."""
     if not cond:
-        raise ValueError(msg)
+        raise ValueError(msg % args if args else msg)
+
+
+_DTYPES = {}
 
 
 def _code_dtypes():
-    torch = _torch()
-    return tuple(d for d in (torch.uint8, getattr(torch, "float8_e4m3fn", None),
-                             getattr(torch, "float8_e5m2", None)) if d is not None)
+    d = _DTYPES.get("codes")
+    if d is None:
+        torch = _torch()
+        d = _DTYPES["codes"] = tuple(x for x in (torch.uint8, getattr(torch, "float8_e4m3fn", None),
+                                                 getattr(torch, "float8_e5m2", None)) if x is not None)
+    return d
 
 
 def _scale_dtypes():
-    torch = _torch()
-    return tuple(d for d in (torch.uint8, getattr(torch, "float8_e8m0fnu", None)) if d is not None)
+    d = _DTYPES.get("scales")
+    if d is None:
+        torch = _torch()
+        d = _DTYPES["scales"] = tuple(x for x in (torch.uint8, getattr(torch, "float8_e8m0fnu", None))
+                                      if x is not None)
+    return d
 
 
 def _is_tensor(t):
@@ -201,42 +212,51 @@ def _is_tensor(t):
 def _matrix(t, name, dtypes, shape):
     """A 2-D tensor of one of `dtypes`, of exactly `shape`, with unit column stride
     (rows may be padded: the row stride is passed as the leading dimension)."""
-    _require(_is_tensor(t), "%s must be a torch tensor" % name)
-    _require(t.dim() == 2, "%s must be 2-D, got %d-D" % (name, t.dim()))
-    _require(t.dtype in dtypes, "%s must have dtype %s, got %s"
-             % (name, " or ".join(str(d) for d in dtypes), t.dtype))
-    _require(tuple(t.shape) == tuple(shape), "%s must have shape %s, got %s"
-             % (name, tuple(shape), tuple(t.shape)))
-    _require(t.shape[1] <= 1 or t.stride(1) == 1, "%s must have unit column stride" % name)
-    _require(t.shape[0] <= 1 or t.stride(0) >= t.shape[1], "%s rows must not overlap" % name)
+    _require(_is_tensor(t), "%s must be a torch tensor", name)
+    sh = t.shape
+    _require(len(sh) == 2, "%s must be 2-D, got %d-D", name, len(sh))
+    if t.dtype not in dtypes:
+        _require(False, "%s must have dtype %s, got %s", name, " or ".join(str(d) for d in dtypes), t.dtype)
+    _require(sh[0] == shape[0] and sh[1] == shape[1], "%s must have shape %s, got %s", name, tuple(shape),
+             tuple(sh))
+    st = t.stride()
+    _require(sh[1] <= 1 or st[1] == 1, "%s must have unit column stride", name)
+    _require(sh[0] <= 1 or st[0] >= sh[1], "%s rows must not overlap", name)
 
 
 def _dense(t, name, dtypes, shape):
     """A contiguous tensor of one of `dtypes` and exactly `shape` (scale, count and
     bitwidth arrays carry no leading dimension)."""
     _matrix(t, name, dtypes, shape)
-    _require(t.is_contiguous(), "%s must be contiguous (dense %s)" % (name, tuple(shape)))
+    _require(t.is_contiguous(), "%s must be contiguous (dense %s)", name, tuple(shape))
 
 
 def _device_of(named):
-    """All tensors on one CUDA device, which must be the current device."""
+    """All tensors on one CUDA device, which must be the current device; returns
+    its index.  (Integer device ids and the raw stream handle below keep the
+    per-call cost of these checks to a few microseconds.)"""
     torch = _torch()
     dev = None
     for name, t in named:
-        _require(t.is_cuda, "%s must be a CUDA tensor, got device %s" % (name, t.device))
+        _require(t.is_cuda, "%s must be a CUDA tensor, got device %s", name, t.device)
+        i = t.get_device()
         if dev is None:
-            dev = t.device
-        _require(t.device == dev, "%s is on %s but %s is on %s" % (name, t.device, named[0][0], dev))
+            dev = i
+        _require(i == dev, "%s is on cuda:%d but %s is on cuda:%d", name, i, named[0][0], dev)
     cur = torch.cuda.current_device()
-    _require(dev.index == cur, "tensors are on %s but the current device is cuda:%d" % (dev, cur))
+    _require(dev == cur, "tensors are on cuda:%d but the current device is cuda:%d", dev, cur)
     return dev
 
 
 def _stream(stream, dev):
+    """The HIP stream handle for device index dev: the given torch stream (which
+    must belong to dev), else dev's current stream."""
     torch = _torch()
-    s = torch.cuda.current_stream(dev) if stream is None else stream
-    _require(s.device == dev, "stream is on %s but the tensors are on %s" % (s.device, dev))
-    return s.cuda_stream
+    if stream is None:
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        return raw(dev) if raw is not None else torch.cuda.current_stream(dev).cuda_stream
+    _require(stream.device.index == dev, "stream is on %s but the tensors are on cuda:%d", stream.device, dev)
+    return stream.cuda_stream
 
 
 def _in_dtype(t):
@@ -251,7 +271,7 @@ def _in_dtype(t):
 def _input(x, name):
     """A float32 / bfloat16 2-D input with unit column stride; returns (rows, cols)."""
     torch = _torch()
-    _require(_is_tensor(x) and x.dim() == 2, "%s must be a 2-D torch tensor" % name)
+    _require(_is_tensor(x) and x.dim() == 2, "%s must be a 2-D torch tensor", name)
     _matrix(x, name, (torch.float32, torch.bfloat16), tuple(x.shape))
     return x.shape
 
@@ -280,7 +300,7 @@ def _check_out(out, out_dtype, M, N):
     torch = _torch()
     if out is None:
         _require(out_dtype in (None, torch.float32, torch.bfloat16),
-                 "out_dtype must be torch.float32 or torch.bfloat16, got %s" % (out_dtype,))
+                 "out_dtype must be torch.float32 or torch.bfloat16, got %s", out_dtype)
     else:
         _matrix(out, "out", (torch.float32, torch.bfloat16), (M, N))
 
@@ -391,7 +411,7 @@ def quantize_mx(x, fmt=E4M3, rule=RULE_FLOOR, counts=True, stream=None):
     """MX 32-element quantization: (q, scales [rows][cols/32], counts [rows][cols/32] or None)."""
     torch = _torch()
     rows, cols = _input(x, "x")
-    _require(cols % 32 == 0, "x must have a multiple of 32 columns, got %d" % cols)
+    _require(cols % 32 == 0, "x must have a multiple of 32 columns, got %d", cols)
     dev = _device_of([("x", x)])
     q = _codes(rows, cols, dev)
     s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
@@ -404,16 +424,16 @@ def quantize_mx(x, fmt=E4M3, rule=RULE_FLOOR, counts=True, stream=None):
 
 def _gemm_operands(a, a_scales, b, b_scales, b_layout, b_scale_mode, scale_dtypes, what):
     """Checks the operands of the block-scaled GEMMs; returns (M, N, K)."""
-    _require(b_layout in (B_NK, B_KN), "b_layout must be B_NK or B_KN, got %r" % (b_layout,))
+    _require(b_layout in (B_NK, B_KN), "b_layout must be B_NK or B_KN, got %r", b_layout)
     _require(b_scale_mode in (SCALE_BLOCK128, SCALE_ROW128),
-             "b_scale_mode must be SCALE_BLOCK128 or SCALE_ROW128, got %r" % (b_scale_mode,))
-    _require(not (b_layout == B_KN and b_scale_mode == SCALE_ROW128), "%s: per-row B scales need B stored [N][K]"
-             % what)
+             "b_scale_mode must be SCALE_BLOCK128 or SCALE_ROW128, got %r", b_scale_mode)
+    _require(not (b_layout == B_KN and b_scale_mode == SCALE_ROW128), "%s: per-row B scales need B stored [N][K]",
+             what)
     _require(_is_tensor(a) and a.dim() == 2, "a must be a 2-D torch tensor")
     _require(_is_tensor(b) and b.dim() == 2, "b must be a 2-D torch tensor")
     M, K = a.shape
     N = b.shape[0] if b_layout == B_NK else b.shape[1]
-    _require(K % 128 == 0, "%s: K must be a multiple of 128, got %d" % (what, K))
+    _require(K % 128 == 0, "%s: K must be a multiple of 128, got %d", what, K)
     codes = _code_dtypes()
     _matrix(a, "a", codes, (M, K))
     _matrix(b, "b", codes, (N, K) if b_layout == B_NK else (K, N))
@@ -455,7 +475,7 @@ def mx_scaled_gemm(a, a_scales, a_fmt, b, b_scales, b_fmt, out_dtype=None, out=N
     _require(_is_tensor(b) and b.dim() == 2, "b must be a 2-D torch tensor")
     M, K = a.shape
     N = b.shape[0]
-    _require(K % 128 == 0, "mx_scaled_gemm: K must be a multiple of 128, got %d" % K)
+    _require(K % 128 == 0, "mx_scaled_gemm: K must be a multiple of 128, got %d", K)
     codes = _code_dtypes()
     _matrix(a, "a", codes, (M, K))
     _matrix(b, "b", codes, (N, K))
