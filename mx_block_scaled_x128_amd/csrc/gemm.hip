@@ -171,7 +171,7 @@ __device__ __forceinline__ void mfma_retire_pad() {
 template <int BM, int BN>
 struct TileLds {
   static constexpr int A_ST = BM * 128, B_ST = BN * 128;
-  static constexpr int STG = 4 * 32 * (BN / 2 * 4 + 16);  // epilogue staging (fp32 strips)
+  static constexpr int STG = 4 * 32 * (BN / 2 * 4);  // epilogue staging (fp32 strips)
   static constexpr int PB = A_ST + B_ST > STG ? A_ST + B_ST : STG;
   static constexpr int SGRP = 2 * 2 * kThreads * 4 * 4;
 };
@@ -730,10 +730,15 @@ __device__ __forceinline__ void gemm_tile(
   // LDS executes one wave's accesses in order, so no barrier is needed.
   auto epilogue = [&](uint8_t* stage_buf) __attribute__((always_inline)) {
     if (!out_bf16) {
-      constexpr int P = WN * 4 + 16;  // bytes per staged row
+      // Unpadded rows, the 16-byte chunk c of row r at chunk c ^ (r & 15):
+      // the 16 rows a write instruction's lane group covers land in 16
+      // different chunks, and a read covers whole rows.  (Without a pad the
+      // 128x128 tile's LDS is 80 KB, two workgroups per compute unit.)
+      constexpr int P = WN * 4;  // bytes per staged row
       static_assert(4 * 32 * P <= PB, "staging fits a buffer");
       uint8_t* stg = stage_buf + wave * (32 * P);
       constexpr int CH = WN / 4;            // 16-byte chunks per row
+      static_assert(CH >= 16, "swizzle within a row");
       constexpr int ROWS_PER = 64 / CH;     // rows per store instruction
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -744,13 +749,13 @@ __device__ __forceinline__ void gemm_tile(
           for (int q = 0; q < 4; ++q) {
             const v4f v = v4f{acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2],
                               acc[mt][nt][4 * q + 3]};
-            *reinterpret_cast<v4f*>(stg + (lane & 31) * P + (nt * 32 + 8 * q + 4 * g) * 4) = v;
+            *reinterpret_cast<v4f*>(stg + (lane & 31) * P + (((nt * 8 + 2 * q + g) ^ (lane & 15)) * 16)) = v;
           }
         const int row0 = m0 + wm * WM + mt * 32;
 #pragma unroll
         for (int it = 0; it < 32 / ROWS_PER; ++it) {
           const int rr = it * ROWS_PER + lane / CH, ch = lane % CH;
-          const v4f v = *reinterpret_cast<const v4f*>(stg + rr * P + ch * 16);
+          const v4f v = *reinterpret_cast<const v4f*>(stg + rr * P + ((ch ^ (rr & 15)) * 16));
           const int m = row0 + rr, n = n0 + wn * WN + ch * 4;
           if (m < M) {
             float* dst = reinterpret_cast<float*>(C) + (int64_t)m * ldc + n;
@@ -828,8 +833,10 @@ __device__ __forceinline__ void gemm_tile(
 #endif
 }
 
+// The 128x128 tile (80 KB of LDS, at most 256 registers) runs two
+// workgroups per compute unit; the others one.
 template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool F32S, bool WS>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(
+__global__ __launch_bounds__(kThreads, (BM == 128 && !F32S) ? 2 : 1) void gemm_bs_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ SA,
     const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ SB, void* __restrict__ C,
     int64_t ldc, int out_bf16, int tiles_m, int tiles_n, int tile_first) {
