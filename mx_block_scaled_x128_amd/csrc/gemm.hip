@@ -834,9 +834,11 @@ __device__ __forceinline__ void gemm_tile(
 }
 
 // The 128x128 tile (80 KB of LDS, at most 256 registers) runs two
-// workgroups per compute unit; the others one.
+// workgroups per compute unit; the others one.  With fp32 scales per column
+// of B (16 scale values per fragment) 256 registers make the K loop spill,
+// so that variant keeps one.
 template <int BM, int BN, int STAGES, int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool F32S, bool WS>
-__global__ __launch_bounds__(kThreads, (BM == 128 && !F32S) ? 2 : 1) void gemm_bs_kernel(
+__global__ __launch_bounds__(kThreads, (BM == 128 && !(F32S && BROW)) ? 2 : 1) void gemm_bs_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ SA,
     const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ SB, void* __restrict__ C,
     int64_t ldc, int out_bf16, int tiles_m, int tiles_n, int tile_first) {
