@@ -107,18 +107,29 @@ class KernelTimer:
 
 
 class ColdTimer(KernelTimer):
-    """Like KernelTimer, but every timed call is preceded by a write of a 512 MiB scrub
-    buffer (twice the 256 MB last-level cache), outside the event pair: the call then
-    finds none of its inputs in the caches."""
+    """Like KernelTimer, but every timed call is preceded, outside the event pair, by a
+    pass over a 512 MiB scrub buffer (twice the 256 MB last-level cache), so that the
+    call finds none of its inputs in the caches.  A read pass (`dirty=False`) leaves the
+    caches full of clean lines; a write pass leaves them full of dirty ones, which the
+    memory system writes back while the timed call runs (its time then includes the
+    write-back of the scrub's own data)."""
 
-    def __init__(self, scrub):
+    def __init__(self, scrub, dirty=False):
+        import torch
         super().__init__()
         self.scrub = scrub
+        self.dirty = dirty
         self.count = 0
+        self.words = scrub.view(torch.int64)
+        self.acc = torch.zeros(1, dtype=torch.int64, device=scrub.device)
 
     def run(self, name, fn):
+        import torch
         self.count += 1
-        self.scrub.fill_(self.count & 0xFF)
+        if self.dirty:
+            self.scrub.fill_(self.count & 0xFF)
+        else:
+            torch.sum(self.words.view(1, -1), dim=1, out=self.acc)
         return super().run(name, fn)
 
 
@@ -139,18 +150,22 @@ class _CaptureTimer(_NoTimer):
 
 
 def context_measurements(step, timer, reps=10):
-    """Median warm and cold (scrubbed) per-call times, the device description and a
-    measured device copy bandwidth, added to the JSON line as context."""
+    """Median warm and cold (scrubbed: clean, then dirty caches) per-call times, the
+    device description and a measured device copy bandwidth, added to the JSON line
+    as context."""
     import torch
-    scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    cold = ColdTimer(scrub)
-    step(cold)  # warm-up of the scrub path
-    torch.cuda.synchronize()
-    cold.pending = []
-    for _ in range(reps):
-        step(cold)
-    torch.cuda.synchronize()
-    cold.collect()
+    scrub = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+    colds = []
+    for dirty in (False, True):
+        cold = ColdTimer(scrub, dirty)
+        step(cold)  # warm-up of the scrub path
+        torch.cuda.synchronize()
+        cold.pending = []
+        for _ in range(reps):
+            step(cold)
+        torch.cuda.synchronize()
+        cold.collect()
+        colds.append(cold)
     n = 256 << 20
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
@@ -166,7 +181,8 @@ def context_measurements(step, timer, reps=10):
     del scrub, src, dst
     props = torch.cuda.get_device_properties(0)
     per = {name: {"us_median": round(timer.median(name) * 1e6, 2),
-                  "us_cold_median": round(cold.median(name) * 1e6, 2)} for name in timer.times}
+                  "us_cold_median": round(colds[0].median(name) * 1e6, 2),
+                  "us_cold_dirty_median": round(colds[1].median(name) * 1e6, 2)} for name in timer.times}
     return per, {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                  "compute_units": props.multi_processor_count, "copy_256MiB_GBs": round(copy_gbs, 1)}
 
@@ -796,7 +812,9 @@ def bench_workload(args):
                       "value: `steps` whole steps launched back to back between two device synchronisations "
                       "(ms_per_step); kernels.us: mean of event-bracketed calls in a second pass of `steps` steps "
                       "(ms_per_step_with_events), on the stream they run on "
-                      "(us_median: median); us_cold_median: each call after a 512 MiB scrub write, medians of 10; "
+                      "(us_median: median); us_cold_median: each call after a 512 MiB scrub read (no input in "
+                      "the caches, which hold clean lines), us_cold_dirty_median: after a 512 MiB scrub write "
+                      "(the caches' dirty lines are written back during the call), medians of 10; "
                       "roofline.achieved: from kernels.<kernel>.us; gemm.us_back_to_back: mean of GEMM calls "
                       "issued back to back between one event pair (operands left in the caches by the previous "
                       "call: context, not the step); ms_per_step_graph: replays of a HIP graph of steps_per_graph "
