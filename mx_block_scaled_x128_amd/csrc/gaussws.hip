@@ -82,7 +82,7 @@ __device__ __forceinline__ uint32_t bf16_rne(float v) {
   return b >> 16;
 }
 
-template <typename InT>
+template <typename InT, bool NT>
 __global__ __launch_bounds__(kThreads) void gaussws_kernel(const InT* __restrict__ w, uint32_t rows, uint32_t cols,
                                                            int64_t ldw, const int8_t* __restrict__ bt, uint32_t nbc,
                                                            uint64_t seed, uint64_t stream_id,
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void gaussws_kernel(const InT* __restrict
   float f[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (cact && r0 + i < rows) load8<false>(w + (int64_t)(r0 + i) * ldw + col, f[i]);
+    if (cact && r0 + i < rows) load8<NT>(w + (int64_t)(r0 + i) * ldw + col, f[i]);
     else
 #pragma unroll
       for (int k = 0; k < 8; ++k) f[i][k] = 0.0f;
@@ -139,12 +139,15 @@ void launch_gaussws(const void* w, int dtype, int64_t rows, int64_t cols, int64_
                     uint64_t seed, uint64_t stream_id, uint16_t* out, int64_t ldo, hipStream_t stream) {
   const uint32_t nbc = (uint32_t)((cols + 31) / 32);
   const dim3 grid((uint32_t)((cols + 255) / 256) * (uint32_t)((rows + 31) / 32));
-  if (dtype == 1)
-    hipLaunchKernelGGL((gaussws_kernel<uint16_t>), grid, dim3(kThreads), 0, stream, (const uint16_t*)w,
-                       (uint32_t)rows, (uint32_t)cols, ldw, bt, nbc, seed, stream_id, out, ldo);
-  else
-    hipLaunchKernelGGL((gaussws_kernel<float>), grid, dim3(kThreads), 0, stream, (const float*)w, (uint32_t)rows,
-                       (uint32_t)cols, ldw, bt, nbc, seed, stream_id, out, ldo);
+  if (dtype == 1) {
+    const auto kern = stream_loads(rows, cols, 2) ? gaussws_kernel<uint16_t, true> : gaussws_kernel<uint16_t, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, (const uint16_t*)w, (uint32_t)rows, (uint32_t)cols,
+                       ldw, bt, nbc, seed, stream_id, out, ldo);
+  } else {
+    const auto kern = stream_loads(rows, cols, 4) ? gaussws_kernel<float, true> : gaussws_kernel<float, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, (const float*)w, (uint32_t)rows, (uint32_t)cols, ldw,
+                       bt, nbc, seed, stream_id, out, ldo);
+  }
 }
 
 }  // namespace mxfp8

@@ -7,6 +7,12 @@
 
 namespace mxfp8 {
 
+// Whether a kernel streams its input with non-temporal loads: inputs of at
+// least 64 MiB (a quarter of the 256 MB last-level cache), read once per call.
+inline uint32_t stream_loads(int64_t rows, int64_t cols, int64_t elem_bytes) {
+  return rows * cols * elem_bytes >= (int64_t(64) << 20) ? 1u : 0u;
+}
+
 // Token-wise 1x128 groups along rows.  cols % 16 == 0.
 void launch_quant_row(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                       uint8_t* q, int64_t ldq, uint8_t* s, hipStream_t stream);

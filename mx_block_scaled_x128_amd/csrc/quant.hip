@@ -122,7 +122,7 @@ __device__ __forceinline__ void store_tile_t(const uint8_t* tile, uint8_t* __res
 // ---------------------------------------------------------------------------
 // F32S: fp32 scales (scale_f32, codes8_div) instead of E8M0 bytes; s then
 // points to floats.
-template <typename InT, int FMT, int U, bool F32S>
+template <typename InT, int FMT, int U, bool F32S, bool NT>
 __global__ __launch_bounds__(kThreads) void quant_row_kernel(
     const InT* __restrict__ x, uint32_t cols, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
     void* __restrict__ s, uint32_t ngroups, uint32_t ipr, uint32_t total_items) {
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(
       grp[u] = g;
       gvalid[u] = item < total_items && g < ngroups;
       act[u] = gvalid[u] && c < cols;
-      if (act[u]) load8<true>(x + (int64_t)r * ldx + c, f[u]);
+      if (act[u]) load8<NT>(x + (int64_t)r * ldx + c, f[u]);
       else zero8(f[u]);
     }
 #pragma unroll
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(
 // stores; each thread writes its 4 tokens' codes of a channel as 4 bytes).
 // ---------------------------------------------------------------------------
 
-template <typename InT, int FMT, bool F32S>
+template <typename InT, int FMT, bool F32S, bool NT>
 __global__ __launch_bounds__(kColThreads) void quant_col_t_kernel(
     const InT* __restrict__ x, uint32_t rows, uint32_t cols, int64_t ldx, uint8_t* __restrict__ qt,
     int64_t ldq, void* __restrict__ st, uint32_t ngt) {
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kColThreads) void quant_col_t_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t r = t0 + tr * 4 + i;
-    if (cact && r < rows) load8<false>(x + (int64_t)r * ldx + c0 + tc * 8, f[i]);
+    if (cact && r < rows) load8<NT>(x + (int64_t)r * ldx + c0 + tc * 8, f[i]);
     else zero8(f[i]);
   }
   uint32_t m[8];
@@ -260,7 +260,7 @@ __device__ __forceinline__ uint32_t max_stride8(uint32_t v) {
   return v > o ? v : o;
 }
 
-template <typename InT, int FMT>
+template <typename InT, int FMT, bool NT>
 __global__ __launch_bounds__(kColThreads) void quant_dual_kernel(
     const InT* __restrict__ x, uint32_t rows, uint32_t cols, int64_t ldx, uint8_t* __restrict__ q,
     int64_t ldq, uint8_t* __restrict__ s, uint8_t* __restrict__ qt, int64_t ldqt, uint8_t* __restrict__ st,
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kColThreads) void quant_dual_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t r = t0 + tr * 4 + i;
-    if (cact && r < rows) load8<false>(x + (int64_t)r * ldx + c0 + tc * 8, f[i]);
+    if (cact && r < rows) load8<NT>(x + (int64_t)r * ldx + c0 + tc * 8, f[i]);
     else zero8(f[i]);
   }
   uint32_t m[8];
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(kColThreads) void quant_dual_kernel(
 // quant_col_t_kernel, amax over the whole tile, both code sets staged in LDS
 // (the padded transposed tile and the swizzled row tile).
 // ---------------------------------------------------------------------------
-template <typename InT, int FMT>
+template <typename InT, int FMT, bool NT>
 __global__ __launch_bounds__(kThreads) void quant_block_dual_kernel(
     const InT* __restrict__ w, uint32_t rows, uint32_t cols, int64_t ldw, uint8_t* __restrict__ q,
     int64_t ldq, uint8_t* __restrict__ s, uint8_t* __restrict__ qt, int64_t ldqt, uint8_t* __restrict__ st,
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void quant_block_dual_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t r = r0 + tr * 8 + i;
-    if (cact && r < rows) load8<false>(w + (int64_t)r * ldw + c0 + tc * 8, f[i]);
+    if (cact && r < rows) load8<NT>(w + (int64_t)r * ldw + c0 + tc * 8, f[i]);
     else zero8(f[i]);
   }
   uint32_t m = 0;
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void quant_block_dual_kernel(
 // then one pass of casts and 8-byte stores.  Input is read from HBM exactly
 // once.
 // ---------------------------------------------------------------------------
-template <typename InT, int FMT, bool F32S>
+template <typename InT, int FMT, bool F32S, bool NT>
 __global__ __launch_bounds__(kBlockThreads) void quant_block_kernel(
     const InT* __restrict__ w, uint32_t rows, uint32_t cols, int64_t ldw, uint8_t* __restrict__ q,
     int64_t ldq, void* __restrict__ s, uint32_t nbc) {
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(kBlockThreads) void quant_block_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t r = r0 + tr * 4 + i;
-    if (cact && r < rows) load8<false>(w + (int64_t)r * ldw + c0 + tc * 8, f[i]);
+    if (cact && r < rows) load8<NT>(w + (int64_t)r * ldw + c0 + tc * 8, f[i]);
     else zero8(f[i]);
   }
   uint32_t m = 0;
@@ -530,8 +530,10 @@ static void row_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ldx,
   const uint32_t ngroups = (uint32_t)((cols + 127) / 128);
   const uint32_t ipr = (ngroups + 3) / 4;
   const uint64_t items = (uint64_t)rows * ipr;
-  hipLaunchKernelGGL((quant_row_kernel<InT, FMT, U, F32S>), dim3(grid_for(items, U)), dim3(kThreads), 0, st,
-                     (const InT*)x, (uint32_t)cols, ldx, q, ldq, s, ngroups, ipr, (uint32_t)items);
+  const auto kern = stream_loads(rows, cols, sizeof(InT)) ? quant_row_kernel<InT, FMT, U, F32S, true>
+                                                          : quant_row_kernel<InT, FMT, U, F32S, false>;
+  hipLaunchKernelGGL(kern, dim3(grid_for(items, U)), dim3(kThreads), 0, st, (const InT*)x, (uint32_t)cols, ldx, q,
+                     ldq, s, ngroups, ipr, (uint32_t)items);
 }
 
 template <bool F32S>
@@ -561,8 +563,10 @@ static void col_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ldx,
                          int64_t ldq, void* st, hipStream_t stream) {
   const uint32_t ngt = (uint32_t)((rows + 127) / 128);
   const dim3 grid((uint32_t)((cols + 127) / 128) * ngt);
-  hipLaunchKernelGGL((quant_col_t_kernel<InT, FMT, F32S>), grid, dim3(kColThreads), 0, stream, (const InT*)x,
-                     (uint32_t)rows, (uint32_t)cols, ldx, qt, ldq, st, ngt);
+  const auto kern = stream_loads(rows, cols, sizeof(InT)) ? quant_col_t_kernel<InT, FMT, F32S, true>
+                                                          : quant_col_t_kernel<InT, FMT, F32S, false>;
+  hipLaunchKernelGGL(kern, grid, dim3(kColThreads), 0, stream, (const InT*)x, (uint32_t)rows, (uint32_t)cols, ldx,
+                     qt, ldq, st, ngt);
 }
 
 template <bool F32S>
@@ -591,8 +595,10 @@ template <typename InT, int FMT>
 static void dual_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
                           uint8_t* s, uint8_t* qt, int64_t ldqt, uint8_t* st, hipStream_t stream) {
   const uint32_t ngc = (uint32_t)((cols + 127) / 128), ngt = (uint32_t)((rows + 127) / 128);
-  hipLaunchKernelGGL((quant_dual_kernel<InT, FMT>), dim3(ngc * ngt), dim3(kColThreads), 0, stream, (const InT*)x,
-                     (uint32_t)rows, (uint32_t)cols, ldx, q, ldq, s, qt, ldqt, st, ngc, ngt);
+  const auto kern = stream_loads(rows, cols, sizeof(InT)) ? quant_dual_kernel<InT, FMT, true>
+                                                          : quant_dual_kernel<InT, FMT, false>;
+  hipLaunchKernelGGL(kern, dim3(ngc * ngt), dim3(kColThreads), 0, stream, (const InT*)x, (uint32_t)rows,
+                     (uint32_t)cols, ldx, q, ldq, s, qt, ldqt, st, ngc, ngt);
 }
 
 void launch_quant_dual(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
@@ -611,8 +617,10 @@ static void block_dual_dispatch(const void* w, int64_t rows, int64_t cols, int64
                                 int64_t ldq, uint8_t* s, uint8_t* qt, int64_t ldqt, uint8_t* st,
                                 hipStream_t stream) {
   const uint32_t nbc = (uint32_t)((cols + 127) / 128), nbr = (uint32_t)((rows + 127) / 128);
-  hipLaunchKernelGGL((quant_block_dual_kernel<InT, FMT>), dim3(nbc * nbr), dim3(kThreads), 0, stream,
-                     (const InT*)w, (uint32_t)rows, (uint32_t)cols, ldw, q, ldq, s, qt, ldqt, st, nbc, nbr);
+  const auto kern = stream_loads(rows, cols, sizeof(InT)) ? quant_block_dual_kernel<InT, FMT, true>
+                                                          : quant_block_dual_kernel<InT, FMT, false>;
+  hipLaunchKernelGGL(kern, dim3(nbc * nbr), dim3(kThreads), 0, stream, (const InT*)w, (uint32_t)rows,
+                     (uint32_t)cols, ldw, q, ldq, s, qt, ldqt, st, nbc, nbr);
 }
 
 void launch_quant_block_dual(const void* w, int dtype, int64_t rows, int64_t cols, int64_t ldw, int fmt,
@@ -632,8 +640,10 @@ static void block_dispatch(const void* w, int64_t rows, int64_t cols, int64_t ld
                            int64_t ldq, void* s, hipStream_t stream) {
   const uint32_t nbc = (uint32_t)((cols + 127) / 128);
   const dim3 grid(nbc * (uint32_t)((rows + 127) / 128));
-  hipLaunchKernelGGL((quant_block_kernel<InT, FMT, F32S>), grid, dim3(kBlockThreads), 0, stream, (const InT*)w,
-                     (uint32_t)rows, (uint32_t)cols, ldw, q, ldq, s, nbc);
+  const auto kern = stream_loads(rows, cols, sizeof(InT)) ? quant_block_kernel<InT, FMT, F32S, true>
+                                                          : quant_block_kernel<InT, FMT, F32S, false>;
+  hipLaunchKernelGGL(kern, grid, dim3(kBlockThreads), 0, stream, (const InT*)w, (uint32_t)rows, (uint32_t)cols,
+                     ldw, q, ldq, s, nbc);
 }
 
 template <bool F32S>
@@ -665,6 +675,8 @@ static void mx_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ldx, 
   const uint32_t nblk = (uint32_t)(cols / 32);
   const uint32_t ipr = (nblk + 15) / 16;
   const uint64_t items = (uint64_t)rows * ipr;
+  // Ordinary loads at every size: non-temporal ones made this kernel 15 %
+  // slower on 64 MiB fp32 tensors.
   hipLaunchKernelGGL((mx_kernel<InT, FMT, RULE, COUNTS, U>), dim3(grid_for(items, U)), dim3(kThreads), 0,
                      stream, (const InT*)x, ldx, q, ldq, s, counts, nblk, ipr, (uint32_t)items);
 }
