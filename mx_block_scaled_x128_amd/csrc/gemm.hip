@@ -910,10 +910,13 @@ inline int device_cus() {
   return n;
 }
 
-// Tile choice: 256x256 (128x128 per wave, the lowest LDS traffic per MFMA) when
-// there are enough tiles to cover the CUs, else 128x128; a short last round
-// of 256x256 tiles runs as 128x128 quadrants.  Building with
-// -DMXFP8_GEMM_TILE=128 or 256 pins one tile size everywhere (for tuning).
+// Tile choice: 128x128 when its tiles fit on the CUs at two per CU (one
+// round), else 256x256 (128x128 per wave, the lowest LDS traffic per MFMA);
+// a short last round of 256x256 tiles runs as 128x128 quadrants.  Measured
+// at M = 4096 (K = 4096): N = 2048 (512 small tiles) 34 us against 43 us for
+// 256x256, N = 2560 (640 small tiles, two rounds of them) 55 against 44 us.
+// Building with -DMXFP8_GEMM_TILE=128 or 256 pins one tile size everywhere
+// (for tuning).
 #ifndef MXFP8_GEMM_TILE
 #define MXFP8_GEMM_TILE 0
 #endif
@@ -922,12 +925,12 @@ void launch_shape(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda
                   const uint8_t* b, int64_t ldb, const uint8_t* sb, void* c, int64_t ldc, int c_dtype,
                   hipStream_t stream) {
   const int bm = (int)((M + 255) / 256), bn = (int)((N + 255) / 256), big_tiles = bm * bn;
+  const int sm = (int)((M + 127) / 128), sn = (int)((N + 127) / 128);
   const int cus = device_cus();
   // The 256-wide tile needs K >= 256: a separate single-K-block drain would
   // make the accumulators spill (merging three exit paths of 256 of them).
-  const bool big = K >= 256 && (MXFP8_GEMM_TILE == 256 || (MXFP8_GEMM_TILE == 0 && big_tiles >= cus));
+  const bool big = K >= 256 && (MXFP8_GEMM_TILE == 256 || (MXFP8_GEMM_TILE == 0 && sm * sn > 2 * cus));
   if (!big) {
-    const int sm = (int)((M + 127) / 128), sn = (int)((N + 127) / 128);
     launch_tile<128, 128, 4, AFMT, BFMT, BKN, BROW, MXS, false, WS>(M, N, K, a, lda, sa, b, ldb, sb, c, ldc, c_dtype,
                                                                    sm, sn, 0, sm * sn, stream);
     return;

@@ -223,6 +223,27 @@ def test_short_last_round_as_quadrants(b_layout, b_scale, bf16_out):
     assert_gemm_close(y[ii, jj], y_s, t_s, bf16_out, "sampled", hw_bound=hb_s, max_over_plain=adversarial_cap(ii.size))
 
 
+@pytest.mark.parametrize("M,N,K", [(2600, 4000, 512), (2600, 3600, 384)])
+def test_partial_round_of_256_tiles(M, N, K):
+    """More 128x128 tiles than fit on the CUs at two each, fewer 256x256 tiles than
+    CUs: one partial round of 256x256 tiles (176 cells, a multiple of 8, so the
+    per-XCD bands apply; and 165 cells, where they do not), ragged in M and N,
+    K = 512 (4-byte scale loads) and K = 384 (odd K-block count, 1-byte loads).
+    N(0, 1) data quantized on the GPU; every output against the oracle at the
+    plain bound, in fp32 and in bf16."""
+    rng = np.random.default_rng(950 + M + N + K)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    aq, a_s = mx.quantize_token(dev(x), mx.E4M3, mx.ROW)
+    bq, b_s = mx.quantize_block(dev(w), mx.E4M3)
+    y32 = mx.block_scaled_gemm(aq, a_s, mx.E4M3, bq, b_s, mx.E4M3, out_dtype=torch.float32)
+    y16 = mx.block_scaled_gemm(aq, a_s, mx.E4M3, bq, b_s, mx.E4M3, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    y_ref, t_ref = oracle.gemm(host(aq), host(a_s), 0, host(bq), host(b_s), 0, threads=8)
+    assert_gemm_close(host(y32), y_ref, t_ref, False, "partial round, fp32")
+    assert_gemm_close(host(y16), y_ref, t_ref, True, "partial round, bf16")
+
+
 def _at_odd_address(t):
     """The same bytes, contiguous, starting one byte into an allocation."""
     buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
