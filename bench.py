@@ -839,7 +839,9 @@ def bench_workload(args):
 def bench_gemm_sweep(args):
     """The block-scaled GEMM at M = 4096 over N and K, bf16 output (and fp32 output at one
     shape), uniformly random finite E4M3 codes with scale bytes in [120, 134]: one round of
-    256x256 tiles at N = 4096 (256 tiles, one per CU), two rounds at N = 8192.  Per shape,
+    256x256 tiles at N = 4096 (256 tiles, one per CU), two rounds at N = 8192; at N = 2048
+    the 512 tiles of 128x128 (two workgroups per CU), at N = 2560 one partial round of 160
+    256x256 tiles (the two sides of the tile-size choice).  Per shape,
     `warmup` calls and then `steps` calls back to back between one event pair (mean per
     call).  A least-squares line through the one-round bf16 points, time = fixed + slope x
     (K / 128), separates the cost of a round that does not scale with K (prologue, output
@@ -849,7 +851,7 @@ def bench_gemm_sweep(args):
     import synth
     M = 4096
     shapes = [(4096, 256, True), (4096, 512, True), (4096, 1536, True), (4096, 3072, True), (4096, 6144, True),
-              (8192, 1536, True), (4096, 1536, False)]
+              (8192, 1536, True), (4096, 1536, False), (2048, 4096, True), (2048, 8192, True), (2560, 4096, True)]
     res = []
     for i, (N, K, bf16) in enumerate(shapes):
         a = torch.from_numpy(synth.random_codes(7000 + 4 * i, (M, K), 0)).cuda()
@@ -882,7 +884,7 @@ def bench_gemm_sweep(args):
             "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(best["us"] / 1e3, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic (random finite codes)",
-            "config": {"workload": "gemmsweep: M=4096, N in {4096, 8192}, K in {256 .. 6144}"},
+            "config": {"workload": "gemmsweep: M=4096, N in {2048, 2560, 4096, 8192}, K in {256 .. 8192}"},
             "sweep": res, "fit_one_round_bf16": {"fixed_us": round(float(fixed), 2),
                                                  "us_per_k_block": round(float(slope), 3)},
             "roofline": {"bound": "mfma", "achieved": best["TFLOP/s"], "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
