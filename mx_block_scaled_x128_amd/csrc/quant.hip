@@ -10,7 +10,9 @@
 // Every kernel reads its input once (16-byte vector loads, 8 elements per
 // lane), reduces amax with DPP inside the wavefront (LDS only where a group
 // spans waves), and writes packed codes (8 bytes per lane) with ordinary
-// stores, which leave them in the last-level cache for the GEMM.
+// stores, which leave them in the last-level cache for the GEMM.  NT (a
+// template parameter, chosen per launch by stream_loads): non-temporal input
+// loads, for inputs of 64 MiB or more.
 #include "device_common.hpp"
 #include "launch.hpp"
 
