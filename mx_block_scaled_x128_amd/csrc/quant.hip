@@ -131,7 +131,9 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t sub = lane & 15;
   const uint32_t slot = lane >> 4;
-  const uint32_t wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  // Known uniform: the item index math (row = item / items per row, addresses)
+  // then runs on the scalar unit.
+  const uint32_t wave = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t nwaves = gridDim.x * (kThreads / 64);
   for (uint32_t it = wave * U; it < total_items; it += nwaves * U) {
     float f[U][8];
@@ -464,7 +466,9 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t sub = lane & 3;
   const uint32_t slot = lane >> 2;
-  const uint32_t wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  // Known uniform: the item index math (row = item / items per row, addresses)
+  // then runs on the scalar unit.
+  const uint32_t wave = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t nwaves = gridDim.x * (kThreads / 64);
   for (uint32_t it = wave * U; it < total_items; it += nwaves * U) {
     float f[U][8];
