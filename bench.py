@@ -66,8 +66,8 @@ def to_dev(a):
 
 
 def oracle_threads():
-    """Host threads for the oracle: the machine's cores, at most 16 (the host share of
-    one GPU on the boxes this runs on)."""
+    """Host threads for the oracle: the machine's cores, at most 16 (a one-GPU share of
+    a multi-GPU host's cores)."""
     return min(16, os.cpu_count() or 1)
 
 
