@@ -76,10 +76,14 @@ __device__ __forceinline__ float rounded_normal(uint32_t u) {
   return (u >> 31) ? -mag : mag;
 }
 
-__device__ __forceinline__ uint32_t bf16_rne(float v) {
-  uint32_t b = __float_as_uint(v);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return b >> 16;
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest-even bf16, packed (lo in bits 0-15):
+// one v_cvt_pk_bf16_f32 (the default round mode is nearest-even; subnormals
+// are kept; a NaN stays a NaN).
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{lo, hi}), v2bf));
 }
 
 template <typename InT, bool NT>
@@ -125,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void gaussws_kernel(const InT* __restrict
     for (int q = 0; q < 4; ++q) {
       const float lo = f[i][2 * q] + rounded_normal((uint32_t)u.v[q]) * scale;
       const float hi = f[i][2 * q + 1] + rounded_normal((uint32_t)(u.v[q] >> 32)) * scale;
-      h[q] = bf16_rne(lo) | (bf16_rne(hi) << 16);
+      h[q] = bf16x2_rne(lo, hi);
     }
     *reinterpret_cast<uint4*>(out + (int64_t)r * ldo + col) = make_uint4(h[0], h[1], h[2], h[3]);
   }

@@ -76,10 +76,14 @@ typedef __attribute__((address_space(3))) v2i lds_v2i;
 
 constexpr int kThreads = 256;  // 4 waves, arranged 2 x 2 over the tile
 
-__device__ __forceinline__ uint32_t bf16_rne(float v) {
-  uint32_t b = __float_as_uint(v);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return b >> 16;
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest-even bf16, packed (lo in bits 0-15):
+// one v_cvt_pk_bf16_f32 (the default round mode is nearest-even; fp32
+// subnormals are kept, and bf16 has fp32's exponent range).
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{lo, hi}), v2bf));
 }
 
 // [rows][128 B] K-block tiles: row r, logical 16-byte chunk c at physical
@@ -782,8 +786,8 @@ __device__ __forceinline__ void gemm_tile(
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             uint2 o;
-            o.x = bf16_rne(acc[mt][nt][4 * q]) | (bf16_rne(acc[mt][nt][4 * q + 1]) << 16);
-            o.y = bf16_rne(acc[mt][nt][4 * q + 2]) | (bf16_rne(acc[mt][nt][4 * q + 3]) << 16);
+            o.x = bf16x2_rne(acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1]);
+            o.y = bf16x2_rne(acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]);
             *reinterpret_cast<uint2*>(stg + (lane & 31) * P + (nt * 32 + 8 * q + 4 * g) * 2) = o;
           }
         const int row0 = m0 + wm * WM + mt * 32;
