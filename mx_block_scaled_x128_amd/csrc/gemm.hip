@@ -857,15 +857,21 @@ __global__ __launch_bounds__(kThreads, (BM == 128 && !(F32S && BROW)) ? 2 : 1) v
 #endif
 }
 
-// 256x256 tiles for cells 0 .. big - 1 (workgroups 0 .. big - 1), then the
-// remaining cells as 128x128 quadrants (the kTailSub workgroups per cell
-// after them), in one launch.  Workgroups start in id order as compute units
-// free up, so the quadrants begin on each compute unit as soon as its last
-// 256x256 tile retires, while that tile's output stores still drain;
-// launched separately they would wait for the whole first kernel to finish.
-// big is a multiple of 8, so both parts keep their per-XCD bands.  (256x128
-// halves instead of quadrants, half as many workgroups, took 3 us longer on
-// the 4096x8960x1536 shape.)
+// The cells past the last full round of 256x256 tiles as 128x128 quadrants
+// (kTailSub workgroups per cell, workgroups 0 .. nq - 1), then cells
+// 0 .. big - 1 as 256x256 tiles (workgroups nq ..), in one launch.
+// Workgroups start in id order as compute units free up: the quadrants run
+// first on most compute units while the rest start 256x256 tiles, so the
+// compute units reach their epilogues at two different times and each
+// burst of output stores is smaller.  Quadrants last, the whole chip wrote
+// its tiles at once, twice, and 64 compute units sat idle in the quadrant
+// round: 4096x8960x1536 took 60.7-61.5 us (bf16 out) and 71.6-72.2 us
+// (fp32 out) that way against 56.2-58.7 and 63.3-65.6 us now,
+// 4096x8960x4096 129.5-130.1 against 120.6-121.3 us (A/B in one process).
+// big is a multiple of 8 and the 256x256 part's ids are offset by the
+// constant nq, which only permutes the XCDs, so it keeps its per-XCD bands.
+// (256x128 halves instead of quadrants, half as many workgroups, took 3 us
+// longer on the 4096x8960x1536 shape.)
 constexpr int kTailSub = 4;
 template <int AFMT, int BFMT, bool BKN, bool BROW, bool MXS, bool WS>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bs_split_tail_kernel(
@@ -878,15 +884,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_split_tail_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[L::PB];
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[L::PB];
   __shared__ __attribute__((aligned(1024))) uint8_t sgrp[L::SGRP];
+  const int nq = (int)gridDim.x - big;
   const int b = blockIdx.x;
-  if (b < big)
+  if (b >= nq)
     gemm_tile<256, 256, 4, AFMT, BFMT, BKN, BROW, MXS, false, WS>(M, N, K, A, lda, SA, B, ldb, SB, C, ldc,
-                                                                  out_bf16, tiles_m, tiles_n, 0, 0, 0, b, big, kbuf0,
-                                                                  kbuf1, sgrp);
+                                                                  out_bf16, tiles_m, tiles_n, 0, 0, 0, b - nq, big,
+                                                                  kbuf0, kbuf1, sgrp);
   else
     gemm_tile<128, 128, 4, AFMT, BFMT, BKN, BROW, MXS, false, WS>(M, N, K, A, lda, SA, B, ldb, SB, C, ldc,
-                                                                  out_bf16, tiles_m, tiles_n, big, 1, 1, b - big,
-                                                                  (int)gridDim.x - big, kbuf0, kbuf1, sgrp);
+                                                                  out_bf16, tiles_m, tiles_n, big, 1, 1, b, nq,
+                                                                  kbuf0, kbuf1, sgrp);
 #endif
 }
 
