@@ -30,6 +30,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--
                        [--cpu-rows R]
 """
 import argparse
+import contextlib
+import gc
 import hashlib
 import json
 import os
@@ -79,15 +81,29 @@ def _check(st, what):
 # ------------------------------------------------------------------------ timing
 
 class KernelTimer:
-    """Event pairs around each launch on the current stream; averages per kernel."""
+    """Event pairs around each launch on the current stream; averages per kernel.  The
+    events come from a pool made (and recorded once) in advance, so that a timed call
+    costs the host two event records and the launch: the host stays ahead of the device,
+    and an event pair does not span a wait for the host."""
 
     def __init__(self):
         self.pending = []
         self.times = {}
+        self.pool = []
+
+    def reserve(self, n):
+        import torch
+        while len(self.pool) < n:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()  # creates the device event now
+            self.pool.append(e)
+
+    def _event(self):
+        import torch
+        return self.pool.pop() if self.pool else torch.cuda.Event(enable_timing=True)
 
     def run(self, name, fn):
-        import torch
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s, e = self._event(), self._event()
         s.record()
         out = fn()
         e.record()
@@ -97,6 +113,7 @@ class KernelTimer:
     def collect(self):
         for name, s, e in self.pending:
             self.times.setdefault(name, []).append(s.elapsed_time(e) * 1e-3)
+            self.pool += [s, e]
         self.pending = []
 
     def mean(self, name):
@@ -270,35 +287,58 @@ def time_plain(step, steps, warmup):
     """`warmup` untimed steps, then `steps` steps launched back to back from Python
     between two device synchronisations, with nothing else on the stream: the host
     enqueues the asynchronous calls far faster than the device runs them, so the wall
-    time is the device's time for the step.  Returns seconds per step."""
+    time is the device's time for the step (Python's garbage collector is held off
+    meanwhile).  Returns seconds per step."""
     import torch
     for _ in range(warmup):
         step(_NoTimer())
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step(_NoTimer())
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    with gc_paused():
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step(_NoTimer())
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    return wall / steps
 
 
 def time_steps(step, steps, warmup):
     """The eager pass with events: `steps` steps launched from Python, each entry point
-    between an event pair.  Returns (seconds per step, timer)."""
+    between an event pair (from the timer's pool), with Python's garbage collector held
+    off during the pass (a collection pause while the device waits for the next launch
+    would count as kernel time).  Returns (seconds per step, timer)."""
     import torch
     timer = KernelTimer()
+    step(timer)  # a warm-up step that counts the step's launches
+    timer.reserve(2 * len(timer.pending) * (warmup + steps))
+    timer.pending = []
     for _ in range(warmup):
         step(timer)
     torch.cuda.synchronize()
     timer.pending = []
     timer.times = {}
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step(timer)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with gc_paused():
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step(timer)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     timer.collect()
     return wall / steps, timer
+
+
+@contextlib.contextmanager
+def gc_paused():
+    """Python's garbage collector off inside the block (no collection first: a pause
+    of the host before the timed steps would leave the device idle long enough to
+    lower its clock)."""
+    was = gc.isenabled()
+    gc.disable()
+    try:
+        yield
+    finally:
+        if was:
+            gc.enable()
 
 
 def recorded_traffic(workload):
