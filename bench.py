@@ -107,12 +107,23 @@ class KernelTimer:
         s.record()
         out = fn()
         e.record()
-        self.pending.append((name, s, e))
+        self.pending.append((name, s, e, 1))
         return out
 
+    def run_many(self, name, fns):
+        """Launches of one kernel issued back to back inside one event pair; each
+        counts as the pair's time divided by their number (a pair per launch would
+        measure the host when it issues launches slower than the device runs them)."""
+        s, e = self._event(), self._event()
+        s.record()
+        outs = [fn() for fn in fns]
+        e.record()
+        self.pending.append((name, s, e, len(fns)))
+        return outs
+
     def collect(self):
-        for name, s, e in self.pending:
-            self.times.setdefault(name, []).append(s.elapsed_time(e) * 1e-3)
+        for name, s, e, n in self.pending:
+            self.times.setdefault(name, []).extend([s.elapsed_time(e) * 1e-3 / n] * n)
             self.pool += [s, e]
         self.pending = []
 
@@ -140,19 +151,29 @@ class ColdTimer(KernelTimer):
         self.words = scrub.view(torch.int64)
         self.acc = torch.zeros(1, dtype=torch.int64, device=scrub.device)
 
-    def run(self, name, fn):
+    def _scrub(self):
         import torch
         self.count += 1
         if self.dirty:
             self.scrub.fill_(self.count & 0xFF)
         else:
             torch.sum(self.words.view(1, -1), dim=1, out=self.acc)
+
+    def run(self, name, fn):
+        self._scrub()
         return super().run(name, fn)
+
+    def run_many(self, name, fns):
+        self._scrub()  # once, before the batch
+        return super().run_many(name, fns)
 
 
 class _NoTimer:
     def run(self, name, fn):
         return fn()
+
+    def run_many(self, name, fns):
+        return [fn() for fn in fns]
 
 
 class _CaptureTimer(_NoTimer):
@@ -164,6 +185,10 @@ class _CaptureTimer(_NoTimer):
     def run(self, name, fn):
         self.fns[name] = fn
         return fn()
+
+    def run_many(self, name, fns):
+        self.fns[name] = fns[-1]
+        return [fn() for fn in fns]
 
 
 def context_measurements(step, timer, reps=10):
@@ -738,10 +763,10 @@ def w_mxstress():
 
     def step(timer):
         stream = torch.cuda.current_stream().cuda_stream
-        for j in range(ntens):
-            _check(timer.run("mx_quant", lambda: mx.mx_quantize(
+        for st in timer.run_many("mx_quant", [lambda j=j: mx.mx_quantize(
                 xs_[j].data_ptr(), mx.F32, R, C, C, mx.E4M3, mx.RULE_FLOOR, q.data_ptr(), C, sc.data_ptr(),
-                cn.data_ptr(), stream)), "mx")
+                cn.data_ptr(), stream) for j in range(ntens)]):
+            _check(st, "mx")
     sizes = {"mx_quant": R * C * 5 + 2 * R * (C // 32)}
 
     def device_stats():
@@ -851,7 +876,8 @@ def bench_workload(args):
                       "steps before each timed pass. "
                       "value: `steps` whole steps launched back to back between two device synchronisations "
                       "(ms_per_step); kernels.us: mean of event-bracketed calls in a second pass of `steps` steps "
-                      "(ms_per_step_with_events), on the stream they run on "
+                      "(ms_per_step_with_events), on the stream they run on (mxstress: one event pair around a step's 64 "
+                      "launches, divided by 64) "
                       "(us_median: median); us_cold_median: each call after a 512 MiB scrub read (no input in "
                       "the caches, which hold clean lines), us_cold_dirty_median: after a 512 MiB scrub write "
                       "(the caches' dirty lines are written back during the call), medians of 10; "
