@@ -193,10 +193,10 @@ def test_end_to_end_quantize_then_gemm_small():
 @pytest.mark.parametrize("bf16_out", [False, True])
 def test_short_last_round_as_quadrants(b_layout, b_scale, bf16_out):
     """17 x 16 cells of 256x256 on 256 CUs: the last 16 cells run as 128x128
-    quadrants after the 256x256 tiles, in the same launch, some of them wholly
-    past the M edge.  The
-    quadrant rows are compared with the oracle in full, the rest on samples
-    (a band across the last full cell row and random points)."""
+    quadrants ahead of the 256x256 tiles, in the same launch, some of them
+    wholly past the M edge.  The quadrant rows are compared with the oracle in
+    full, the rest on samples (a band across the last full cell row and random
+    points)."""
     M, N, K = 256 * 16 + 100, 256 * 16 - 30, 256
     seed = 77 + 10 * b_layout + b_scale
     a = synth.random_codes(seed, (M, K), 0)
@@ -221,6 +221,31 @@ def test_short_last_round_as_quadrants(b_layout, b_scale, bf16_out):
     y_s, t_s = oracle.gemm_elems(a, sa, 0, b, sb_store, 1, ii, jj, b_layout, b_scale, threads=8)
     hb_s = alignment_bound_fn(a, sa, 0, b_nk, sb, 1, b_scale, ii=ii, jj=jj)
     assert_gemm_close(y[ii, jj], y_s, t_s, bf16_out, "sampled", hw_bound=hb_s, max_over_plain=adversarial_cap(ii.size))
+
+
+def test_one_cell_tail_as_quadrants():
+    """257 cells of 256x256 on 256 CUs: one cell past the full round runs as four
+    quadrants (workgroups 0-3, a count that is no multiple of the 8 XCDs), the
+    256x256 tiles after them.  N = 216 (one partial cell column), K = 384 (three
+    K blocks, one-byte scale loads).  The quadrant cell's rows in full, the rest
+    on samples."""
+    M, N, K = 256 * 257, 216, 384
+    a = synth.random_codes(91, (M, K), 0)
+    b = synth.random_codes(92, (N, K), 0)
+    sa = synth.random_scale_bytes(93, (M, K // 128))
+    sb = synth.random_scale_bytes(94, (-(-N // 128), K // 128))
+    y = run_gemm(a, sa, 0, b, sb, 0, mx.B_NK, mx.SCALE_BLOCK128, False)
+    r0 = 256 * 256
+    y_ref, t_ref = oracle.gemm(a[r0:], sa[r0:], 0, b, sb, 0, threads=8)
+    hb = alignment_bound_fn(a[r0:], sa[r0:], 0, b, sb, 0, mx.SCALE_BLOCK128)
+    assert_gemm_close(y[r0:], y_ref, t_ref, False, "quadrant cell", hw_bound=hb,
+                      max_over_plain=adversarial_cap(y_ref.size))
+    rng = np.random.default_rng(95)
+    ii = rng.integers(0, r0, 4096)
+    jj = rng.integers(0, N, ii.size)
+    y_s, t_s = oracle.gemm_elems(a, sa, 0, b, sb, 0, ii, jj, threads=8)
+    hb_s = alignment_bound_fn(a, sa, 0, b, sb, 0, mx.SCALE_BLOCK128, ii=ii, jj=jj)
+    assert_gemm_close(y[ii, jj], y_s, t_s, False, "sampled", hw_bound=hb_s, max_over_plain=adversarial_cap(ii.size))
 
 
 @pytest.mark.parametrize("M,N,K", [(2600, 4000, 512), (2600, 3600, 384)])
