@@ -36,7 +36,6 @@
 
 #include <stdint.h>
 
-#include <atomic>
 
 // One translation unit can hold every kernel (MXFP8_GEMM_FMT undefined), or
 // the build compiles this file once per (A format, B format) pair,
@@ -905,20 +904,6 @@ void launch_tile(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
   hipLaunchKernelGGL((gemm_bs_kernel<BM, BN, STAGES, AFMT, BFMT, BKN, BROW, MXS, F32S, WS>), dim3(cells),
                      dim3(kThreads), 0, stream, (int)M, (int)N, (int)K, a, lda, sa, b, ldb, sb, c, ldc,
                      c_dtype == 1 ? 1 : 0, tiles_m, tiles_n, tile_first);
-}
-
-// Compute units of the current device (cached per device; concurrent first
-// calls store the same value).
-inline int device_cus() {
-  static std::atomic<int> cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cus[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
 }
 
 // Tile choice: 128x128 when its tiles fit on the CUs at two per CU (one

@@ -5,7 +5,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace mxfp8 {
+
+// Compute units of the current device (cached per device; concurrent first
+// calls store the same value).
+inline int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // Whether a kernel streams its input with non-temporal loads: inputs of at
 // least 64 MiB (a quarter of the 256 MB last-level cache), read once per call.

@@ -404,50 +404,130 @@ __global__ __launch_bounds__(kThreads) void quant_block_dual_kernel(
 // then one pass of casts and 8-byte stores.  Input is read from HBM exactly
 // once.
 // ---------------------------------------------------------------------------
-template <typename InT, int FMT, bool F32S, bool NT>
+// Raw input of 8 elements (bf16: one 16-byte word; fp32: two), converted
+// when used, so a prefetched tile costs 4 (bf16) or 8 registers per row.
+template <typename InT> struct Raw8;
+template <> struct Raw8<uint16_t> { nt_u32x4 v; };
+template <> struct Raw8<float> { nt_f32x4 a, b; };
+template <bool NT>
+__device__ __forceinline__ void raw_load(const uint16_t* p, Raw8<uint16_t>& r) {
+  r.v = NT ? __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p)) : *reinterpret_cast<const nt_u32x4*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void raw_load(const float* p, Raw8<float>& r) {
+  r.a = NT ? __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p)) : *reinterpret_cast<const nt_f32x4*>(p);
+  r.b = NT ? __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p + 4))
+           : *reinterpret_cast<const nt_f32x4*>(p + 4);
+}
+__device__ __forceinline__ void raw_zero(Raw8<uint16_t>& r) { r.v = nt_u32x4{0, 0, 0, 0}; }
+__device__ __forceinline__ void raw_zero(Raw8<float>& r) { r.a = nt_f32x4{0, 0, 0, 0}; r.b = r.a; }
+__device__ __forceinline__ void raw_f8(const Raw8<uint16_t>& r, float (&f)[8]) {
+  f[0] = bf16_lo(r.v.x); f[1] = bf16_hi(r.v.x); f[2] = bf16_lo(r.v.y); f[3] = bf16_hi(r.v.y);
+  f[4] = bf16_lo(r.v.z); f[5] = bf16_hi(r.v.z); f[6] = bf16_lo(r.v.w); f[7] = bf16_hi(r.v.w);
+}
+// Max of |x| bits over the 8 elements, from the raw words.
+__device__ __forceinline__ uint32_t raw_absmax(const Raw8<uint16_t>& r) {
+  const uint32_t a = max((r.v.x << 16) & 0x7FFFFFFFu, r.v.x & 0x7FFF0000u);
+  const uint32_t b = max((r.v.y << 16) & 0x7FFFFFFFu, r.v.y & 0x7FFF0000u);
+  const uint32_t c = max((r.v.z << 16) & 0x7FFFFFFFu, r.v.z & 0x7FFF0000u);
+  const uint32_t d = max((r.v.w << 16) & 0x7FFFFFFFu, r.v.w & 0x7FFF0000u);
+  return max(max(a, b), max(c, d));
+}
+__device__ __forceinline__ uint32_t raw_absmax(const Raw8<float>& r) {
+  float f[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = max(m, abs_bits(f[j]));
+  return m;
+}
+__device__ __forceinline__ void raw_f8(const Raw8<float>& r, float (&f)[8]) {
+  f[0] = r.a.x; f[1] = r.a.y; f[2] = r.a.z; f[3] = r.a.w;
+  f[4] = r.b.x; f[5] = r.b.y; f[6] = r.b.z; f[7] = r.b.w;
+}
+
+// PIPE: each workgroup takes tiles blockIdx.x, + gridDim.x, ... and loads
+// its next tile before the current one's reduction, barrier and stores, so
+// its loads stay in flight across them (72 registers: 7 waves per SIMD,
+// three workgroups per CU).  Otherwise one tile per workgroup (28 registers,
+// four workgroups per CU): the fp32-scale variant, whose divisions made the
+// pipelined form slower.
+template <typename InT, int FMT, bool F32S, bool NT, bool PIPE>
 __global__ __launch_bounds__(kBlockThreads) void quant_block_kernel(
     const InT* __restrict__ w, uint32_t rows, uint32_t cols, int64_t ldw, uint8_t* __restrict__ q,
-    int64_t ldq, void* __restrict__ s, uint32_t nbc) {
-  __shared__ uint32_t red[kBlockThreads / 64];
+    int64_t ldq, void* __restrict__ s, uint32_t nbc, uint32_t ntiles) {
+  __shared__ uint32_t red[2][kBlockThreads / 64];
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t tc = lane & 15;               // column chunk: columns tc*8 .. tc*8+7
   const uint32_t tr = (lane >> 4) + 4 * wv;    // row chunk: rows tr*4 .. tr*4+3
-  const TileXY b = tile_xy(nbc);
-  const uint32_t r0 = b.y * 128, c0 = b.x * 128;
-  const bool cact = c0 + tc * 8 < cols;
-  float f[4][8];
+  auto load_tile = [&](uint32_t t, Raw8<InT> (&rr)[4]) __attribute__((always_inline)) {
+    const uint32_t by = t / nbc, bx = t - by * nbc;
+    const uint32_t r0 = by * 128, c0 = bx * 128;
+    const bool cact = c0 + tc * 8 < cols;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t r = r0 + tr * 4 + i;
-    if (cact && r < rows) load8<NT>(w + (int64_t)r * ldw + c0 + tc * 8, f[i]);
-    else zero8(f[i]);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t r = r0 + tr * 4 + i;
+      if (cact && r < rows) raw_load<NT>(w + (int64_t)r * ldw + c0 + tc * 8, rr[i]);
+      else raw_zero(rr[i]);
+    }
+  };
+  auto process = [&](uint32_t t, const Raw8<InT> (&rr)[4], int par) __attribute__((always_inline)) {
+    const uint32_t by = t / nbc, bx = t - by * nbc;
+    const uint32_t r0 = by * 128, c0 = bx * 128;
+    const bool cact = c0 + tc * 8 < cols;
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, raw_absmax(rr[i]));
+    m = max_wave(m);
+    if (lane == 0) red[par][wv] = m;
+    __syncthreads();
+    m = max(max(max(red[par][0], red[par][1]), max(red[par][2], red[par][3])),
+            max(max(red[par][4], red[par][5]), max(red[par][6], red[par][7])));
+    if constexpr (F32S) {
+      const float sf = scale_f32<FMT>(m);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t r = r0 + tr * 4 + i;
+        float f[8];
+        raw_f8(rr[i], f);
+        if (cact && r < rows) store_codes(q + (int64_t)r * ldq + c0 + tc * 8, codes8_div<FMT>(f, sf));
+      }
+      if (tid == 0) static_cast<float*>(s)[(int64_t)by * nbc + bx] = sf;
+    } else {
+      const int e = scale_exp_ceil<FMT>(m);
+      const float sc = pow2_neg(e);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t r = r0 + tr * 4 + i;
+        float f[8];
+        raw_f8(rr[i], f);
+        if (cact && r < rows) store_codes(q + (int64_t)r * ldq + c0 + tc * 8, codes8<FMT>(f, sc));
+      }
+      if (tid == 0) static_cast<uint8_t*>(s)[(int64_t)by * nbc + bx] = (uint8_t)(e + 127);
+    }
+  };
+  // Two register sets alternate (a loop body of two tiles), and so do the
+  // two halves of red: a wave that still reads one half cannot be overtaken
+  // by writes into it, which come two tiles (and a barrier) later.
+  Raw8<InT> ra[4];
+  uint32_t t = blockIdx.x;
+  load_tile(t, ra);
+  if constexpr (!PIPE) {
+    process(t, ra, 0);
+    return;
   }
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m = max(m, abs_bits(f[i][j]));
-  m = max_wave(m);
-  if (lane == 0) red[wv] = m;
-  __syncthreads();
-  m = max(max(max(red[0], red[1]), max(red[2], red[3])), max(max(red[4], red[5]), max(red[6], red[7])));
-  if constexpr (F32S) {
-    const float sf = scale_f32<FMT>(m);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t r = r0 + tr * 4 + i;
-      if (cact && r < rows) store_codes(q + (int64_t)r * ldq + c0 + tc * 8, codes8_div<FMT>(f[i], sf));
-    }
-    if (tid == 0) static_cast<float*>(s)[(int64_t)b.y * nbc + b.x] = sf;
-  } else {
-    const int e = scale_exp_ceil<FMT>(m);
-    const float sc = pow2_neg(e);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t r = r0 + tr * 4 + i;
-      if (cact && r < rows) store_codes(q + (int64_t)r * ldq + c0 + tc * 8, codes8<FMT>(f[i], sc));
-    }
-    if (tid == 0) static_cast<uint8_t*>(s)[(int64_t)b.y * nbc + b.x] = (uint8_t)(e + 127);
+  Raw8<InT> rb[4];
+  const uint32_t step = gridDim.x;
+  for (;;) {
+    uint32_t tn = t + step;
+    if (tn < ntiles) load_tile(tn, rb);
+    process(t, ra, 0);
+    if (tn >= ntiles) break;
+    t = tn;
+    tn = t + step;
+    if (tn < ntiles) load_tile(tn, ra);
+    process(t, rb, 1);
+    if (tn >= ntiles) break;
+    t = tn;
   }
 }
 
@@ -645,11 +725,18 @@ template <typename InT, int FMT, bool F32S>
 static void block_dispatch(const void* w, int64_t rows, int64_t cols, int64_t ldw, uint8_t* q,
                            int64_t ldq, void* s, hipStream_t stream) {
   const uint32_t nbc = (uint32_t)((cols + 127) / 128);
-  const dim3 grid(nbc * (uint32_t)((rows + 127) / 128));
-  const auto kern = stream_loads(rows, cols, sizeof(InT)) ? quant_block_kernel<InT, FMT, F32S, true>
-                                                          : quant_block_kernel<InT, FMT, F32S, false>;
+  const uint32_t ntiles = nbc * (uint32_t)((rows + 127) / 128);
+  // Pipelined: tiles per workgroup as few as let every workgroup be resident
+  // at once (three per CU with bf16 input, two with fp32, whose prefetched
+  // tile takes twice the registers), spread evenly.
+  constexpr bool PIPE = !F32S;
+  const uint32_t slots = (sizeof(InT) == 2 ? 3u : 2u) * (uint32_t)device_cus();
+  const uint32_t per = PIPE ? (ntiles + slots - 1) / slots : 1;
+  const dim3 grid((ntiles + per - 1) / per);
+  const auto kern = stream_loads(rows, cols, sizeof(InT)) ? quant_block_kernel<InT, FMT, F32S, true, PIPE>
+                                                          : quant_block_kernel<InT, FMT, F32S, false, PIPE>;
   hipLaunchKernelGGL(kern, grid, dim3(kBlockThreads), 0, stream, (const InT*)w, (uint32_t)rows, (uint32_t)cols,
-                     ldw, q, ldq, s, nbc);
+                     ldw, q, ldq, s, nbc, ntiles);
 }
 
 template <bool F32S>
