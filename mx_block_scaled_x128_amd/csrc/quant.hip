@@ -174,6 +174,55 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(
   }
 }
 
+// Raw input of 8 elements (bf16: one 16-byte word; fp32: two), converted
+// when used, so a prefetched tile costs 4 (bf16) or 8 registers per row.
+template <typename InT> struct Raw8;
+template <> struct Raw8<uint16_t> { nt_u32x4 v; };
+template <> struct Raw8<float> { nt_f32x4 a, b; };
+template <bool NT>
+__device__ __forceinline__ void raw_load(const uint16_t* p, Raw8<uint16_t>& r) {
+  r.v = NT ? __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p)) : *reinterpret_cast<const nt_u32x4*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void raw_load(const float* p, Raw8<float>& r) {
+  r.a = NT ? __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p)) : *reinterpret_cast<const nt_f32x4*>(p);
+  r.b = NT ? __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p + 4))
+           : *reinterpret_cast<const nt_f32x4*>(p + 4);
+}
+__device__ __forceinline__ void raw_zero(Raw8<uint16_t>& r) { r.v = nt_u32x4{0, 0, 0, 0}; }
+__device__ __forceinline__ void raw_zero(Raw8<float>& r) { r.a = nt_f32x4{0, 0, 0, 0}; r.b = r.a; }
+__device__ __forceinline__ void raw_f8(const Raw8<uint16_t>& r, float (&f)[8]) {
+  f[0] = bf16_lo(r.v.x); f[1] = bf16_hi(r.v.x); f[2] = bf16_lo(r.v.y); f[3] = bf16_hi(r.v.y);
+  f[4] = bf16_lo(r.v.z); f[5] = bf16_hi(r.v.z); f[6] = bf16_lo(r.v.w); f[7] = bf16_hi(r.v.w);
+}
+// Max of |x| bits over the 8 elements, from the raw words.
+__device__ __forceinline__ uint32_t raw_absmax(const Raw8<uint16_t>& r) {
+  const uint32_t a = max((r.v.x << 16) & 0x7FFFFFFFu, r.v.x & 0x7FFF0000u);
+  const uint32_t b = max((r.v.y << 16) & 0x7FFFFFFFu, r.v.y & 0x7FFF0000u);
+  const uint32_t c = max((r.v.z << 16) & 0x7FFFFFFFu, r.v.z & 0x7FFF0000u);
+  const uint32_t d = max((r.v.w << 16) & 0x7FFFFFFFu, r.v.w & 0x7FFF0000u);
+  return max(max(a, b), max(c, d));
+}
+__device__ __forceinline__ uint32_t raw_absmax(const Raw8<float>& r) {
+  float f[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = max(m, abs_bits(f[j]));
+  return m;
+}
+__device__ __forceinline__ void raw_f8(const Raw8<float>& r, float (&f)[8]) {
+  f[0] = r.a.x; f[1] = r.a.y; f[2] = r.a.z; f[3] = r.a.w;
+  f[4] = r.b.x; f[5] = r.b.y; f[6] = r.b.z; f[7] = r.b.w;
+}
+
+// Element j (0..7; a compile-time constant after unrolling) of raw words.
+__device__ __forceinline__ float raw_elem(const Raw8<uint16_t>& r, int j) {
+  const uint32_t wd = j < 2 ? r.v.x : j < 4 ? r.v.y : j < 6 ? r.v.z : r.v.w;
+  return (j & 1) ? bf16_hi(wd) : bf16_lo(wd);
+}
+__device__ __forceinline__ float raw_elem(const Raw8<float>& r, int j) {
+  return j < 4 ? r.a[j] : r.b[j - 4];
+}
 // ---------------------------------------------------------------------------
 // 128-token groups down columns, codes written transposed (token axis
 // contiguous).  One workgroup of 8 waves per 128 tokens x 128 channels tile:
@@ -197,21 +246,21 @@ __global__ __launch_bounds__(kColThreads) void quant_col_t_kernel(
   const TileXY b = tile_xy((cols + 127) >> 7);
   const uint32_t c0 = b.x * 128, t0 = b.y * 128;
   const bool cact = c0 + tc * 8 < cols;
-  float f[4][8];  // [token][channel]
+  // The input stays in its raw words (bf16: 4 registers per token), each
+  // element converted where it is used: holding 32 fp32 values instead made
+  // the kernel 4 % slower (11 % with fp32 scales).
+  Raw8<InT> rr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t r = t0 + tr * 4 + i;
-    if (cact && r < rows) load8<NT>(x + (int64_t)r * ldx + c0 + tc * 8, f[i]);
-    else zero8(f[i]);
+    if (cact && r < rows) raw_load<NT>(x + (int64_t)r * ldx + c0 + tc * 8, rr[i]);
+    else raw_zero(rr[i]);
   }
   uint32_t m[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t a = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a = max(a, abs_bits(f[i][j]));
-    m[j] = max_oct(a);
-  }
+  for (int j = 0; j < 8; ++j)
+    m[j] = max_oct(max(max(abs_bits(raw_elem(rr[0], j)), abs_bits(raw_elem(rr[1], j))),
+                       max(abs_bits(raw_elem(rr[2], j)), abs_bits(raw_elem(rr[3], j)))));
   if ((lane & 7) == 0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) red[w & 3][tc * 8 + j] = m[j];
@@ -232,13 +281,15 @@ __global__ __launch_bounds__(kColThreads) void quant_col_t_kernel(
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
+    const float f0 = raw_elem(rr[0], j), f1 = raw_elem(rr[1], j), f2 = raw_elem(rr[2], j),
+                f3 = raw_elem(rr[3], j);  // tokens 0..3 of channel j
     uint32_t o;
     if constexpr (F32S) {
       const float sf = __int_as_float(exps[tc * 8 + j]);
-      o = cvt4_div<FMT>(f[0][j], f[1][j], f[2][j], f[3][j], sf);
+      o = cvt4_div<FMT>(f0, f1, f2, f3, sf);
     } else {
       const float sc = pow2_neg(exps[tc * 8 + j]);
-      o = cvt4<FMT>(f[0][j] * sc, f[1][j] * sc, f[2][j] * sc, f[3][j] * sc);
+      o = cvt4<FMT>(f0 * sc, f1 * sc, f2 * sc, f3 * sc);
     }
     *reinterpret_cast<uint32_t*>(tile + (tc * 8 + j) * kColPitch + tr * 4) = o;
   }
@@ -404,47 +455,6 @@ __global__ __launch_bounds__(kThreads) void quant_block_dual_kernel(
 // then one pass of casts and 8-byte stores.  Input is read from HBM exactly
 // once.
 // ---------------------------------------------------------------------------
-// Raw input of 8 elements (bf16: one 16-byte word; fp32: two), converted
-// when used, so a prefetched tile costs 4 (bf16) or 8 registers per row.
-template <typename InT> struct Raw8;
-template <> struct Raw8<uint16_t> { nt_u32x4 v; };
-template <> struct Raw8<float> { nt_f32x4 a, b; };
-template <bool NT>
-__device__ __forceinline__ void raw_load(const uint16_t* p, Raw8<uint16_t>& r) {
-  r.v = NT ? __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p)) : *reinterpret_cast<const nt_u32x4*>(p);
-}
-template <bool NT>
-__device__ __forceinline__ void raw_load(const float* p, Raw8<float>& r) {
-  r.a = NT ? __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p)) : *reinterpret_cast<const nt_f32x4*>(p);
-  r.b = NT ? __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p + 4))
-           : *reinterpret_cast<const nt_f32x4*>(p + 4);
-}
-__device__ __forceinline__ void raw_zero(Raw8<uint16_t>& r) { r.v = nt_u32x4{0, 0, 0, 0}; }
-__device__ __forceinline__ void raw_zero(Raw8<float>& r) { r.a = nt_f32x4{0, 0, 0, 0}; r.b = r.a; }
-__device__ __forceinline__ void raw_f8(const Raw8<uint16_t>& r, float (&f)[8]) {
-  f[0] = bf16_lo(r.v.x); f[1] = bf16_hi(r.v.x); f[2] = bf16_lo(r.v.y); f[3] = bf16_hi(r.v.y);
-  f[4] = bf16_lo(r.v.z); f[5] = bf16_hi(r.v.z); f[6] = bf16_lo(r.v.w); f[7] = bf16_hi(r.v.w);
-}
-// Max of |x| bits over the 8 elements, from the raw words.
-__device__ __forceinline__ uint32_t raw_absmax(const Raw8<uint16_t>& r) {
-  const uint32_t a = max((r.v.x << 16) & 0x7FFFFFFFu, r.v.x & 0x7FFF0000u);
-  const uint32_t b = max((r.v.y << 16) & 0x7FFFFFFFu, r.v.y & 0x7FFF0000u);
-  const uint32_t c = max((r.v.z << 16) & 0x7FFFFFFFu, r.v.z & 0x7FFF0000u);
-  const uint32_t d = max((r.v.w << 16) & 0x7FFFFFFFu, r.v.w & 0x7FFF0000u);
-  return max(max(a, b), max(c, d));
-}
-__device__ __forceinline__ uint32_t raw_absmax(const Raw8<float>& r) {
-  float f[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
-  uint32_t m = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) m = max(m, abs_bits(f[j]));
-  return m;
-}
-__device__ __forceinline__ void raw_f8(const Raw8<float>& r, float (&f)[8]) {
-  f[0] = r.a.x; f[1] = r.a.y; f[2] = r.a.z; f[3] = r.a.w;
-  f[4] = r.b.x; f[5] = r.b.y; f[6] = r.b.z; f[7] = r.b.w;
-}
-
 // PIPE: each workgroup takes tiles blockIdx.x, + gridDim.x, ... and loads
 // its next tile before the current one's reduction, barrier and stores, so
 // its loads stay in flight across them (72 registers: 7 waves per SIMD,
