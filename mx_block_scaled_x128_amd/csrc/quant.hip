@@ -331,32 +331,24 @@ __global__ __launch_bounds__(kColThreads) void quant_dual_kernel(
   const TileXY b = tile_xy(ngc);
   const uint32_t c0 = b.x * 128, t0 = b.y * 128;
   const bool cact = c0 + tc * 8 < cols;
-  float f[4][8];  // [token][channel]
+  Raw8<InT> rr[4];  // [token], raw words, converted where used
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t r = t0 + tr * 4 + i;
-    if (cact && r < rows) load8<NT>(x + (int64_t)r * ldx + c0 + tc * 8, f[i]);
-    else zero8(f[i]);
+    if (cact && r < rows) raw_load<NT>(x + (int64_t)r * ldx + c0 + tc * 8, rr[i]);
+    else raw_zero(rr[i]);
   }
   uint32_t m[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t a = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a = max(a, abs_bits(f[i][j]));
-    m[j] = max_oct(a);
-  }
+  for (int j = 0; j < 8; ++j)
+    m[j] = max_oct(max(max(abs_bits(raw_elem(rr[0], j)), abs_bits(raw_elem(rr[1], j))),
+                       max(abs_bits(raw_elem(rr[2], j)), abs_bits(raw_elem(rr[3], j)))));
   if ((lane & 7) == 0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) red[w & 3][tc * 8 + j] = m[j];
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t a = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) a = max(a, abs_bits(f[i][j]));
-    m[i] = max_stride8(a);
-  }
+  for (int i = 0; i < 4; ++i) m[i] = max_stride8(raw_absmax(rr[i]));
   if ((lane >> 3) == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) rred[w >> 2][tr * 4 + i] = m[i];
@@ -380,12 +372,15 @@ __global__ __launch_bounds__(kColThreads) void quant_dual_kernel(
   for (int j = 0; j < 8; ++j) {
     const float sc = pow2_neg(exps[tc * 8 + j]);
     *reinterpret_cast<uint32_t*>(tile + (tc * 8 + j) * kColPitch + tr * 4) =
-        cvt4<FMT>(f[0][j] * sc, f[1][j] * sc, f[2][j] * sc, f[3][j] * sc);
+        cvt4<FMT>(raw_elem(rr[0], j) * sc, raw_elem(rr[1], j) * sc, raw_elem(rr[2], j) * sc,
+                  raw_elem(rr[3], j) * sc);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint2*>(rtile + row_tile_offset(tr * 4 + i, tc)) =
-        codes8<FMT>(f[i], pow2_neg(rexps[tr * 4 + i]));
+  for (int i = 0; i < 4; ++i) {
+    float f[8];
+    raw_f8(rr[i], f);
+    *reinterpret_cast<uint2*>(rtile + row_tile_offset(tr * 4 + i, tc)) = codes8<FMT>(f, pow2_neg(rexps[tr * 4 + i]));
+  }
   __syncthreads();
   store_tile_t<kColThreads>(tile, qt, ldqt, c0, t0, cols, rows, tid);
   store_row_tile<kColThreads>(rtile, q, ldq, t0, c0, rows, cols, tid);
@@ -411,18 +406,16 @@ __global__ __launch_bounds__(kThreads) void quant_block_dual_kernel(
   const TileXY b = tile_xy(nbc);
   const uint32_t c0 = b.x * 128, r0 = b.y * 128;
   const bool cact = c0 + tc * 8 < cols;
-  float f[8][8];  // [row][column]
+  Raw8<InT> rr[8];  // [row], raw words, converted where used
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t r = r0 + tr * 8 + i;
-    if (cact && r < rows) load8<NT>(w + (int64_t)r * ldw + c0 + tc * 8, f[i]);
-    else zero8(f[i]);
+    if (cact && r < rows) raw_load<NT>(w + (int64_t)r * ldw + c0 + tc * 8, rr[i]);
+    else raw_zero(rr[i]);
   }
   uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m = max(m, abs_bits(f[i][j]));
+  for (int i = 0; i < 8; ++i) m = max(m, raw_absmax(rr[i]));
   m = max_wave(m);
   if (lane == 0) red[wv] = m;
   __syncthreads();
@@ -432,13 +425,18 @@ __global__ __launch_bounds__(kThreads) void quant_block_dual_kernel(
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     uint2 o;
-    o.x = cvt4<FMT>(f[0][j] * sc, f[1][j] * sc, f[2][j] * sc, f[3][j] * sc);
-    o.y = cvt4<FMT>(f[4][j] * sc, f[5][j] * sc, f[6][j] * sc, f[7][j] * sc);
+    o.x = cvt4<FMT>(raw_elem(rr[0], j) * sc, raw_elem(rr[1], j) * sc, raw_elem(rr[2], j) * sc,
+                    raw_elem(rr[3], j) * sc);
+    o.y = cvt4<FMT>(raw_elem(rr[4], j) * sc, raw_elem(rr[5], j) * sc, raw_elem(rr[6], j) * sc,
+                    raw_elem(rr[7], j) * sc);
     *reinterpret_cast<uint2*>(tile + (tc * 8 + j) * kColPitch + tr * 8) = o;
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<uint2*>(rtile + row_tile_offset(tr * 8 + i, tc)) = codes8<FMT>(f[i], sc);
+  for (int i = 0; i < 8; ++i) {
+    float f[8];
+    raw_f8(rr[i], f);
+    *reinterpret_cast<uint2*>(rtile + row_tile_offset(tr * 8 + i, tc)) = codes8<FMT>(f, sc);
+  }
   if (tid == 0) {
     s[(int64_t)b.y * nbc + b.x] = (uint8_t)(e + 127);
     st[(int64_t)b.x * nbr + b.y] = (uint8_t)(e + 127);
