@@ -456,9 +456,9 @@ __global__ __launch_bounds__(kThreads) void quant_block_dual_kernel(
 // PIPE: each workgroup takes tiles blockIdx.x, + gridDim.x, ... and loads
 // its next tile before the current one's reduction, barrier and stores, so
 // its loads stay in flight across them (72 registers: 7 waves per SIMD,
-// three workgroups per CU).  Otherwise one tile per workgroup (28 registers,
-// four workgroups per CU): the fp32-scale variant, whose divisions made the
-// pipelined form slower.
+// three workgroups per CU).  Otherwise one tile per workgroup (four
+// workgroups per CU): inputs of at most one round of tiles, and the
+// fp32-scale variant, whose divisions made the pipelined form slower.
 template <typename InT, int FMT, bool F32S, bool NT, bool PIPE>
 __global__ __launch_bounds__(kBlockThreads) void quant_block_kernel(
     const InT* __restrict__ w, uint32_t rows, uint32_t cols, int64_t ldw, uint8_t* __restrict__ q,
@@ -734,15 +734,22 @@ static void block_dispatch(const void* w, int64_t rows, int64_t cols, int64_t ld
                            int64_t ldq, void* s, hipStream_t stream) {
   const uint32_t nbc = (uint32_t)((cols + 127) / 128);
   const uint32_t ntiles = nbc * (uint32_t)((rows + 127) / 128);
-  // Pipelined: tiles per workgroup as few as let every workgroup be resident
-  // at once (three per CU with bf16 input, two with fp32, whose prefetched
-  // tile takes twice the registers), spread evenly.
-  constexpr bool PIPE = !F32S;
-  const uint32_t slots = (sizeof(InT) == 2 ? 3u : 2u) * (uint32_t)device_cus();
-  const uint32_t per = PIPE ? (ntiles + slots - 1) / slots : 1;
+  // Pipelined when the tiles outnumber the workgroups one round of the
+  // one-tile form holds (four per CU): then tiles per workgroup as few as
+  // let every workgroup be resident at once (three per CU with bf16 input,
+  // two with fp32, whose prefetched tile takes twice the registers), spread
+  // evenly.  (Fewer tiles, e.g. 840 for a 8960x1536 weight, ran 11 % slower
+  // pipelined at two per workgroup.)
+  const uint32_t cus = (uint32_t)device_cus();
+  const bool pipe = !F32S && ntiles > 4 * cus;
+  const uint32_t slots = (sizeof(InT) == 2 ? 3u : 2u) * cus;
+  const uint32_t per = pipe ? (ntiles + slots - 1) / slots : 1;
   const dim3 grid((ntiles + per - 1) / per);
-  const auto kern = stream_loads(rows, cols, sizeof(InT)) ? quant_block_kernel<InT, FMT, F32S, true, PIPE>
-                                                          : quant_block_kernel<InT, FMT, F32S, false, PIPE>;
+  const bool nt = stream_loads(rows, cols, sizeof(InT));
+  const auto kern = pipe ? (nt ? quant_block_kernel<InT, FMT, F32S, true, !F32S>
+                               : quant_block_kernel<InT, FMT, F32S, false, !F32S>)
+                         : (nt ? quant_block_kernel<InT, FMT, F32S, true, false>
+                               : quant_block_kernel<InT, FMT, F32S, false, false>);
   hipLaunchKernelGGL(kern, grid, dim3(kBlockThreads), 0, stream, (const InT*)w, (uint32_t)rows, (uint32_t)cols,
                      ldw, q, ldq, s, nbc, ntiles);
 }
